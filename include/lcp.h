@@ -1,0 +1,206 @@
+/*
+ * lcp.h - C ABI of the MI355X (gfx950) learnable-channel-permutation library.
+ *
+ * One LCP step on one linear layer, as defined on the pages "PermLLM: Learnable
+ * Channel Permutation for N:M Sparse Large Language Models" (summary of arXiv
+ * 2510.10136; cited below as [PermLLM]) and the blog post "PermLLM: 动态通道置换
+ * 优化N:M稀疏大模型" (cited as [blog]):
+ *
+ *   logits L (nb x B x B, fp32) --Sinkhorn--> P (soft block permutations)
+ *   W_hat = W P_B,  S_hat = S P_B with S = |W| . ||X_col||_2   (importance)
+ *   M = N:M top-N of S_hat per row and group of M permuted positions
+ *   W_tilde = (W_hat . M) P_B^T,  D = W - W_tilde,  R = D X^T,  E = ||R||_F
+ *   backward: dE/dL through the block permutation and the unrolled Sinkhorn,
+ *   with the mask held constant.
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are row-major. W is Cout x Cin (like a linear layer), X is
+ *     T x Cin (tokens x channels). Block b covers channels [bB, (b+1)B).
+ *   - P_b[j][k]: row j is source channel bB+j, column k is permuted position
+ *     bB+k; so W_hat[:, bB+k] = sum_j W[:, bB+j] P_b[j][k].
+ *   - Every pointer argument is a device pointer owned by the caller, except
+ *     the lcp_layer / lcp_cfg / lcp_timing structs and size_t* outputs, which
+ *     live in host memory. The library never allocates, frees or synchronises,
+ *     holds no global mutable state and is reentrant. Work is enqueued on the
+ *     given HIP stream (a hipStream_t passed as void*; NULL = null stream) and
+ *     runs asynchronously.
+ *   - Inputs are never written. Outputs are fully overwritten.
+ *   - All arguments are validated before the first launch: an error code means
+ *     nothing was enqueued and nothing written. Results are deterministic
+ *     (no atomics in reductions): equal inputs give bitwise-equal outputs.
+ *   - Sizes are limited to what 32-bit element indices of one matrix hold
+ *     (rows * cols < 2^31).
+ */
+#ifndef LCP_H
+#define LCP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LCP_OK             0
+#define LCP_E_INVAL       -1  /* null pointer, non-positive size, Cin % B, B % M,
+                                 N outside [1, M-1], iters < 1, tau not finite
+                                 or <= 0, Cin % 32 for mask words            */
+#define LCP_E_UNSUPPORTED -2  /* B not in {32, 64, 128}, M not in {4, 8},
+                                 unknown dtype, or a dtype/mode combination
+                                 the library does not implement              */
+#define LCP_E_WORKSPACE   -3  /* workspace smaller than the size query says,
+                                 or not 256-byte aligned                      */
+#define LCP_E_HIP         -4  /* a kernel launch reported a HIP error         */
+
+typedef enum lcp_dtype {
+  LCP_F32 = 0,   /* IEEE binary32 */
+  LCP_BF16 = 1   /* bfloat16 (upper half of binary32), round-to-nearest-even */
+} lcp_dtype;
+
+/* One layer and its calibration data (host struct holding device pointers). */
+typedef struct lcp_layer {
+  const void*  W;      /* [cout][cin], dtype                                  */
+  const void*  X;      /* [T][cin], dtype                                     */
+  const void*  Xt;     /* BF16 layers: [cin][lcp_xt_pitch(T)] bf16, written by
+                          lcp_layer_init (X transposed, zero beyond T); used
+                          by the backward. May be NULL for F32 layers.        */
+  const float* norms;  /* [cin] ||X[:, j]||_2, written by lcp_layer_init      */
+  lcp_dtype    dtype;
+  int          cout, cin, T;
+  int          B;      /* block size, 32, 64 or 128; cin % B == 0            */
+} lcp_layer;
+
+/* Hyper-parameters of one step. */
+typedef struct lcp_cfg {
+  int   iters;  /* Sinkhorn iterations L >= 1 (one = row step then column step) */
+  float tau;    /* temperature > 0                                              */
+  int   N, M;   /* keep N of every M; M in {4, 8}, 1 <= N < M, B % M == 0       */
+} lcp_cfg;
+
+/* Optional per-kernel timing hooks: hipEvent_t handles (as void*) recorded on
+ * the step's stream immediately before (start[i]) and after (stop[i]) kernel i
+ * of the step. NULL entries are skipped; a NULL lcp_timing* records nothing.
+ * Forward kernels: 0 Sinkhorn, 1 permute+mask+unpermute, 2 error GEMM,
+ * 3 error finalisation. Backward kernels: 0 dD GEMM, 1 block adjoint,
+ * 2 Sinkhorn adjoint. */
+typedef struct lcp_timing {
+  void* start[8];
+  void* stop[8];
+} lcp_timing;
+
+/* Static description of a status code. */
+const char* lcp_status_string(int code);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int lcp_version(void);
+
+/* ---------------------------------------------------------------------------
+ * lcp_sinkhorn - soft permutations P = S_L(L / tau), batched over nb blocks.
+ * [PermLLM] Method 1: S_0(X) = exp(X), S_i(X) = T_c(T_r(S_{i-1}(X))), with the
+ * log-domain form of [blog] section 2.2 (subtract the row log-sum-exp, then the
+ * column log-sum-exp, each iteration; exp at the end).
+ *   logits: [nb][B][B] fp32 in;  P: [nb][B][B] fp32 out (may alias logits).
+ *   B in {32, 64, 128}; iters >= 1; tau finite and > 0.
+ */
+int lcp_sinkhorn(const float* logits, float* P, int nb, int B, int iters,
+                 float tau, void* stream);
+
+/* lcp_sinkhorn_bwd - reverse pass of lcp_sinkhorn: given dE/dP (fp32
+ * [nb][B][B]) returns dE/dlogits (fp32 [nb][B][B]). The forward iterations are
+ * recomputed from the logits; the derivative of each normalisation follows
+ * from [PermLLM] Method 1 by the chain rule. dlogits must not alias dP. */
+int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B,
+                     int iters, float tau, float* dlogits, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * lcp_colnorm - norms[j] = ||X[:, j]||_2 over the T tokens, fp32 accumulation.
+ * The column norm is the activation factor of Wanda's importance, the one-shot
+ * method [PermLLM] integrates with (its formula is not printed there).
+ *   X: [T][cin] in dtype dt;  norms: [cin] fp32 out.
+ */
+int lcp_colnorm(const void* X, lcp_dtype dt, int T, int cin, float* norms,
+                void* stream);
+
+/* Row pitch (elements) of the transposed activations Xt and of the internal
+ * residual R: T rounded up to a multiple of 64. Returns -1 for T <= 0. */
+int lcp_xt_pitch(int T);
+
+/* lcp_layer_init - per-layer setup, constant across LCP steps on one layer:
+ * column norms and, for BF16, Xt[c][t] = X[t][c] (t < T) and 0 for
+ * T <= t < lcp_xt_pitch(T).
+ *   X: [T][cin] dtype in; norms: [cin] fp32 out; Xt: bf16 [cin][pitch] out
+ *   (required for BF16, ignored and may be NULL for F32). cin % 32 == 0. */
+int lcp_layer_init(const void* X, lcp_dtype dt, int T, int cin, float* norms,
+                   void* Xt, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * lcp_permute - block-wise permutation of the columns of A ([PermLLM]
+ * Method 3: P_B = diag(P_1 .. P_nb), W_hat_B = W P_B; and the permuted
+ * importance S_hat = S P_B of the integration formula).
+ *   out[:, bB+k] = sum_j At[:, bB+j] * Pb[j][k]   with Pb = P_b, or Pb = P_b^T
+ *   when transposeP != 0; At = A, or At = |A| * colscale[col] when colscale is
+ *   non-NULL (importance mode).
+ *   A: [rows][cin] adt; P: [nb][B][B] fp32; out: [rows][cin] odt.
+ *   Importance mode requires odt == LCP_F32 and computes with float32-accurate
+ *   accumulation. BF16 A in plain mode rounds P to bf16 as the MFMA operand.
+ */
+int lcp_permute(const void* A, lcp_dtype adt, int rows, int cin,
+                const float* colscale, const float* P, int B, int transposeP,
+                void* out, lcp_dtype odt, void* stream);
+
+/* lcp_nm_mask - N:M mask from scores ([PermLLM] integration formula:
+ * argmax_M sum (M . S_hat)_{i, kM:(k+1)M}; [blog] 2.1: keep the N largest of
+ * every M consecutive positions). For every row and group g of positions
+ * gM .. gM+M-1, position k is kept iff
+ *   #{j in g : s_j > s_k} + #{j in g, j < k : s_j == s_k} < N,
+ * i.e. ties go to the lower position, NaN ranks as -inf and -0 == +0.
+ *   scores: [rows][cin] fp32; bits: [rows][cin/32] uint32 out, bit (k mod 32)
+ *   of word k/32 is position k, 1 = kept. cin % 32 == 0, M in {4, 8}. */
+int lcp_nm_mask(const float* scores, int rows, int cin, int N, int M,
+                uint32_t* bits, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * lcp_error - output error of a pruned weight on the calibration tokens:
+ *   *err = ||(W - Wt) X^T||_F   (fp32 scalar written to device memory).
+ * The [PermLLM] task definition asks for the permuted, pruned weight whose
+ * layer outputs stay closest to the dense layer's; this is that distance.
+ *   W, Wt: [cout][cin] dt; X: [T][cin] dt; err: 1 fp32 out;
+ *   R_out (nullable): the residual (W - Wt) X^T, [cout][lcp_xt_pitch(T)] in dt
+ *   (columns T .. pitch-1 are zero). BF16 computes D = W - Wt in fp32, rounds
+ *   it to bf16 and multiplies with bf16 MFMA and fp32 accumulation; the norm
+ *   is taken over the fp32 accumulators. ws: lcp_error_workspace_bytes bytes. */
+int lcp_error_workspace_bytes(int cout, int cin, int T, lcp_dtype dt,
+                              size_t* bytes);
+int lcp_error(const void* W, const void* Wt, const void* X, lcp_dtype dt,
+              int cout, int cin, int T, float* err, void* R_out, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Full step. The workspace carries the forward's saved state (P, Sinkhorn
+ * offsets, mask bits, residual R, E) to the backward; it must not be touched
+ * between lcp_step_fwd and the matching lcp_step_bwd, and one workspace
+ * serves one step in flight at a time.
+ */
+int lcp_step_workspace_bytes(int cout, int cin, int T, int B, int iters,
+                             lcp_dtype dt, size_t* bytes);
+
+/* lcp_step_fwd - Sinkhorn, permute, importance, N:M mask, un-permute,
+ * difference, error GEMM: *err = E. Optional copies: P_out [nb][B][B] fp32,
+ * bits_out [cout][cin/32] uint32 (the mask in permuted positions). */
+int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c,
+                 void* ws, size_t ws_bytes, float* err, float* P_out,
+                 uint32_t* bits_out, const lcp_timing* tm, void* stream);
+
+/* lcp_step_bwd - dlogits = dE/dlogits ([nb][B][B] fp32) with the mask of the
+ * matching lcp_step_fwd held constant; zero when E == 0. Needs L->Xt for BF16
+ * layers. */
+int lcp_step_bwd(const lcp_layer* L, const float* logits, const lcp_cfg* c,
+                 void* ws, size_t ws_bytes, float* dlogits,
+                 const lcp_timing* tm, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCP_H */

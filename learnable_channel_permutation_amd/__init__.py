@@ -1,0 +1,60 @@
+"""MI355X (gfx950) learnable channel permutation (LCP) step.
+
+The computation lives in liblcp.so (HIP kernels behind the C ABI of
+include/lcp.h); this package only binds it (``_lib``) and wraps the
+per-layer buffers in a small session object. Importing fails if the library
+has not been built.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (LCP_BF16, LCP_F32, LcpError, lcp_colnorm, lcp_error,  # noqa: F401
+                   lcp_error_workspace_bytes, lcp_layer_init, lcp_nm_mask, lcp_permute,
+                   lcp_sinkhorn, lcp_sinkhorn_bwd, lcp_step_bwd, lcp_step_fwd,
+                   lcp_step_workspace_bytes, lcp_xt_pitch, make_cfg, make_layer, make_timing)
+
+__all__ = ["LayerSession", "LcpError"] + [n for n in _lib.EXPORTS if n.startswith("lcp_")]
+
+
+class LayerSession:
+    """Device buffers for repeated LCP steps on one layer.
+
+    Holds W and X (caller tensors on one GPU), the per-layer setup written by
+    lcp_layer_init (column norms; X transposed for bf16 layers) and one step
+    workspace sized by lcp_step_workspace_bytes.
+    """
+
+    def __init__(self, W, X, B, iters, tau, N, M, stream=None):
+        if W.device != X.device or W.dtype != X.dtype:
+            raise ValueError("W and X must share device and dtype")
+        self.W, self.X = W, X
+        self.B, self.iters, self.tau, self.N, self.M = B, iters, tau, N, M
+        cout, cin = W.shape
+        T = X.shape[0]
+        dev = W.device
+        self.norms = torch.empty(cin, dtype=torch.float32, device=dev)
+        self.Xt = None
+        if W.dtype == torch.bfloat16:
+            self.Xt = torch.empty((cin, lcp_xt_pitch(T)), dtype=torch.bfloat16, device=dev)
+        nbytes = lcp_step_workspace_bytes(cout, cin, T, B, iters, _lib.dtype_code(W))
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.err = torch.empty(1, dtype=torch.float32, device=dev)
+        self.layer = make_layer(W, X, self.norms, B, self.Xt)
+        self.cfg = make_cfg(iters, tau, N, M)
+        self.init(stream)
+
+    def init(self, stream=None):
+        """Per-layer setup (column norms, transposed X)."""
+        lcp_layer_init(self.X, self.norms, self.Xt, stream=stream)
+
+    def forward(self, logits, P_out=None, bits_out=None, timing=None, stream=None):
+        lcp_step_fwd(self.layer, logits, self.cfg, self.ws, self.err, P_out, bits_out, timing, stream)
+        return self.err
+
+    def backward(self, logits, dlogits=None, timing=None, stream=None):
+        if dlogits is None:
+            dlogits = torch.empty_like(logits)
+        lcp_step_bwd(self.layer, logits, self.cfg, self.ws, dlogits, timing, stream)
+        return dlogits

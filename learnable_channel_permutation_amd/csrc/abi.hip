@@ -1,0 +1,328 @@
+// C ABI of liblcp: argument validation, workspace layout and the order of the
+// kernels of one LCP step. Every check runs before the first launch, so an
+// error return means nothing was enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/lcp.h"
+#include "kernels.h"
+
+using namespace lcp;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxIterB = 8192;   // iters * B bound (Sinkhorn offsets kept in LDS)
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool good_dtype(lcp_dtype d) { return d == LCP_F32 || d == LCP_BF16; }
+inline size_t esize(lcp_dtype d) { return d == LCP_BF16 ? 2 : 4; }
+inline bool good_B(int B) { return B == 32 || B == 64 || B == 128; }
+inline bool fits_i32(long long a, long long b) { return a > 0 && b > 0 && a * b < (1LL << 31); }
+inline bool good_tau(float tau) { return isfinite(tau) && tau > 0.f; }
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int pitch_of(int T) { return (T + 63) / 64 * 64; }
+
+struct StepLayout {
+  size_t P, off, bits, D, R, part, E, adj, total;
+  int nb, pitch, nparts, chunks;
+};
+
+StepLayout step_layout(int cout, int cin, int T, int B, int iters, lcp_dtype dt) {
+  StepLayout L{};
+  L.nb = cin / B;
+  L.pitch = pitch_of(T);
+  L.nparts = gemm_error_parts(cout, L.pitch, dt == LCP_BF16);
+  L.chunks = adjoint_chunks(cout, L.nb, B);
+  size_t o = 0;
+  L.P = o;    o += align_up((size_t)L.nb * B * B * 4);
+  L.off = o;  o += align_up((size_t)L.nb * iters * 2 * B * 4);
+  L.bits = o; o += align_up((size_t)cout * (cin / 32) * 4);
+  L.D = o;    o += align_up((size_t)cout * cin * esize(dt));
+  L.R = o;    o += align_up((size_t)cout * L.pitch * esize(dt));
+  L.part = o; o += align_up((size_t)L.nparts * 4);
+  L.E = o;    o += align_up(4);
+  L.adj = o;  o += align_up((size_t)L.chunks * L.nb * B * B * 4);
+  L.total = o;
+  return L;
+}
+
+int check_step_args(const lcp_layer* L, const float* logits, const lcp_cfg* c) {
+  if (!L || !logits || !c) return LCP_E_INVAL;
+  if (!good_dtype(L->dtype)) return LCP_E_UNSUPPORTED;
+  if (!L->W || !L->X || !L->norms) return LCP_E_INVAL;
+  if (L->cout <= 0 || L->cin <= 0 || L->T <= 0 || L->B <= 0) return LCP_E_INVAL;
+  if (c->iters < 1 || !good_tau(c->tau)) return LCP_E_INVAL;
+  if (c->M <= 0 || c->N < 1 || c->N >= c->M) return LCP_E_INVAL;
+  if (L->cin % L->B != 0 || L->B % c->M != 0) return LCP_E_INVAL;
+  if (!good_B(L->B)) return LCP_E_UNSUPPORTED;
+  if (c->M != 4 && c->M != 8) return LCP_E_UNSUPPORTED;
+  if ((long long)c->iters * L->B > kMaxIterB) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(L->cout, L->cin) || !fits_i32(L->T, L->cin) || !fits_i32(L->cout, pitch_of(L->T)) ||
+      !fits_i32(L->cin, pitch_of(L->T)))
+    return LCP_E_INVAL;
+  if (!aligned16(L->W) || !aligned16(L->X) || !aligned16(logits)) return LCP_E_INVAL;
+  return LCP_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return LCP_E_INVAL;
+  if (((uintptr_t)ws % kAlign) != 0 || ws_bytes < need) return LCP_E_WORKSPACE;
+  return LCP_OK;
+}
+
+struct Timer {
+  const lcp_timing* tm;
+  hipStream_t s;
+  void start(int i) const { if (tm && tm->start[i]) (void)hipEventRecord((hipEvent_t)tm->start[i], s); }
+  void stop(int i) const { if (tm && tm->stop[i]) (void)hipEventRecord((hipEvent_t)tm->stop[i], s); }
+};
+
+#define LCP_RUN(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return LCP_E_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* lcp_status_string(int code) {
+  switch (code) {
+    case LCP_OK: return "ok";
+    case LCP_E_INVAL: return "invalid argument";
+    case LCP_E_UNSUPPORTED: return "unsupported configuration";
+    case LCP_E_WORKSPACE: return "workspace too small or misaligned";
+    case LCP_E_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int lcp_version(void) { return 100; }
+
+int lcp_xt_pitch(int T) { return T > 0 ? pitch_of(T) : -1; }
+
+int lcp_sinkhorn(const float* logits, float* P, int nb, int B, int iters, float tau, void* stream) {
+  if (!logits || !P || nb <= 0 || B <= 0 || iters < 1 || !good_tau(tau)) return LCP_E_INVAL;
+  if (!good_B(B)) return LCP_E_UNSUPPORTED;
+  if ((long long)iters * B > kMaxIterB) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(nb, (long long)B * B) || !aligned16(logits) || !aligned16(P)) return LCP_E_INVAL;
+  LCP_RUN(launch_sinkhorn_fwd(logits, P, nullptr, nb, B, iters, tau, S(stream)));
+  return LCP_OK;
+}
+
+int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B, int iters, float tau,
+                     float* dlogits, void* stream) {
+  if (!logits || !dP || !dlogits || nb <= 0 || B <= 0 || iters < 1 || !good_tau(tau)) return LCP_E_INVAL;
+  if (dlogits == dP) return LCP_E_INVAL;
+  if (!good_B(B)) return LCP_E_UNSUPPORTED;
+  if ((long long)iters * B > kMaxIterB) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(nb, (long long)B * B) || !aligned16(logits) || !aligned16(dP) || !aligned16(dlogits))
+    return LCP_E_INVAL;
+  LCP_RUN(launch_sinkhorn_bwd(logits, dP, 1, 0, nullptr, dlogits, nb, B, iters, tau, S(stream)));
+  return LCP_OK;
+}
+
+int lcp_colnorm(const void* X, lcp_dtype dt, int T, int cin, float* norms, void* stream) {
+  if (!X || !norms || T <= 0 || cin <= 0) return LCP_E_INVAL;
+  if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(T, cin) || !aligned16(X)) return LCP_E_INVAL;
+  if (dt == LCP_BF16) {
+    if (cin % 8) return LCP_E_INVAL;
+    LCP_RUN(launch_layer_init_bf16((const uint16_t*)X, T, cin, pitch_of(T), norms, nullptr, S(stream)));
+  } else {
+    LCP_RUN(launch_colnorm_f32((const float*)X, T, cin, norms, S(stream)));
+  }
+  return LCP_OK;
+}
+
+int lcp_layer_init(const void* X, lcp_dtype dt, int T, int cin, float* norms, void* Xt, void* stream) {
+  if (!X || !norms || T <= 0 || cin <= 0) return LCP_E_INVAL;
+  if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
+  if (cin % 32 || !fits_i32(T, cin) || !fits_i32(cin, pitch_of(T)) || !aligned16(X)) return LCP_E_INVAL;
+  if (dt == LCP_BF16) {
+    if (!Xt || !aligned16(Xt)) return LCP_E_INVAL;
+    LCP_RUN(launch_layer_init_bf16((const uint16_t*)X, T, cin, pitch_of(T), norms, (uint16_t*)Xt, S(stream)));
+  } else {
+    LCP_RUN(launch_colnorm_f32((const float*)X, T, cin, norms, S(stream)));
+  }
+  return LCP_OK;
+}
+
+int lcp_permute(const void* A, lcp_dtype adt, int rows, int cin, const float* colscale, const float* P,
+                int B, int transposeP, void* out, lcp_dtype odt, void* stream) {
+  if (!A || !P || !out || rows <= 0 || cin <= 0 || B <= 0) return LCP_E_INVAL;
+  if (!good_dtype(adt) || !good_dtype(odt)) return LCP_E_UNSUPPORTED;
+  if (cin % B) return LCP_E_INVAL;
+  if (!good_B(B)) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(rows, cin) || !aligned16(A) || !aligned16(out) || !aligned16(P)) return LCP_E_INVAL;
+  const int mode = colscale ? PERM_IMPORTANCE : PERM_PLAIN;
+  if (mode == PERM_IMPORTANCE && odt != LCP_F32) return LCP_E_UNSUPPORTED;
+  if (adt == LCP_F32 && odt != LCP_F32) return LCP_E_UNSUPPORTED;
+  if (adt == LCP_BF16) {
+    LCP_RUN(launch_permute_bf16((const uint16_t*)A, rows, cin, colscale, P, B, transposeP ? 1 : 0, mode, out,
+                                odt == LCP_F32, nullptr, 0, 4, S(stream)));
+  } else {
+    LCP_RUN(launch_permute_f32((const float*)A, rows, cin, colscale, P, B, transposeP ? 1 : 0, mode,
+                               (float*)out, nullptr, 0, 4, S(stream)));
+  }
+  return LCP_OK;
+}
+
+int lcp_nm_mask(const float* scores, int rows, int cin, int N, int M, uint32_t* bits, void* stream) {
+  if (!scores || !bits || rows <= 0 || cin <= 0 || M <= 0) return LCP_E_INVAL;
+  if (N < 1 || N >= M || cin % 32) return LCP_E_INVAL;
+  if (M != 4 && M != 8) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(rows, cin) || !aligned16(scores)) return LCP_E_INVAL;
+  LCP_RUN(launch_nm_mask(scores, rows, cin, N, M, bits, S(stream)));
+  return LCP_OK;
+}
+
+int lcp_error_workspace_bytes(int cout, int cin, int T, lcp_dtype dt, size_t* bytes) {
+  if (!bytes || cout <= 0 || cin <= 0 || T <= 0) return LCP_E_INVAL;
+  if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(cout, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  const int pitch = pitch_of(T);
+  *bytes = align_up((size_t)cout * cin * esize(dt)) + align_up((size_t)cout * pitch * esize(dt)) +
+           align_up((size_t)gemm_error_parts(cout, pitch, dt == LCP_BF16) * 4) + align_up(4);
+  return LCP_OK;
+}
+
+int lcp_error(const void* W, const void* Wt, const void* X, lcp_dtype dt, int cout, int cin, int T,
+              float* err, void* R_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !Wt || !X || !err || cout <= 0 || cin <= 0 || T <= 0) return LCP_E_INVAL;
+  if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
+  if (cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  if (!aligned16(W) || !aligned16(Wt) || !aligned16(X) || (R_out && !aligned16(R_out))) return LCP_E_INVAL;
+  size_t need = 0;
+  int rc = lcp_error_workspace_bytes(cout, cin, T, dt, &need);
+  if (rc != LCP_OK) return rc;
+  rc = check_ws(ws, ws_bytes, need);
+  if (rc != LCP_OK) return rc;
+  const int pitch = pitch_of(T);
+  char* base = (char*)ws;
+  void* D = base;
+  char* Rp = base + align_up((size_t)cout * cin * esize(dt));
+  float* part = (float*)(Rp + align_up((size_t)cout * pitch * esize(dt)));
+  const int nparts = gemm_error_parts(cout, pitch, dt == LCP_BF16);
+  float* Ews = (float*)((char*)part + align_up((size_t)nparts * 4));
+  void* R = R_out ? R_out : (void*)Rp;
+  hipStream_t s = S(stream);
+  LCP_RUN(launch_diff(W, Wt, cout * cin, dt == LCP_BF16, D, s));
+  if (dt == LCP_BF16)
+    LCP_RUN(launch_gemm_error_bf16((const uint16_t*)D, cin, (const uint16_t*)X, cin, cout, T, pitch, cin,
+                                   (uint16_t*)R, pitch, part, s));
+  else
+    LCP_RUN(launch_gemm_error_f32((const float*)D, cin, (const float*)X, cin, cout, T, pitch, cin, (float*)R,
+                                  pitch, part, s));
+  LCP_RUN(launch_error_finalize(part, nparts, Ews, err, s));
+  return LCP_OK;
+}
+
+int lcp_step_workspace_bytes(int cout, int cin, int T, int B, int iters, lcp_dtype dt, size_t* bytes) {
+  if (!bytes || cout <= 0 || cin <= 0 || T <= 0 || B <= 0 || iters < 1) return LCP_E_INVAL;
+  if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
+  if (cin % B) return LCP_E_INVAL;
+  if (!good_B(B)) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(cout, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  *bytes = step_layout(cout, cin, T, B, iters, dt).total;
+  return LCP_OK;
+}
+
+int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void* ws, size_t ws_bytes,
+                 float* err, float* P_out, uint32_t* bits_out, const lcp_timing* tm, void* stream) {
+  int rc = check_step_args(L, logits, c);
+  if (rc != LCP_OK) return rc;
+  if (!err) return LCP_E_INVAL;
+  const StepLayout Ly = step_layout(L->cout, L->cin, L->T, L->B, c->iters, L->dtype);
+  rc = check_ws(ws, ws_bytes, Ly.total);
+  if (rc != LCP_OK) return rc;
+
+  char* base = (char*)ws;
+  float* P = (float*)(base + Ly.P);
+  float* off = (float*)(base + Ly.off);
+  uint32_t* bits = (uint32_t*)(base + Ly.bits);
+  void* D = base + Ly.D;
+  void* R = base + Ly.R;
+  float* part = (float*)(base + Ly.part);
+  float* Ews = (float*)(base + Ly.E);
+  hipStream_t s = S(stream);
+  const Timer tmr{tm, s};
+  const bool bf = L->dtype == LCP_BF16;
+
+  tmr.start(0);
+  LCP_RUN(launch_sinkhorn_fwd(logits, P, off, Ly.nb, L->B, c->iters, c->tau, s));
+  tmr.stop(0);
+  tmr.start(1);
+  if (bf)
+    LCP_RUN(launch_permute_bf16((const uint16_t*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, PERM_FWD, D, 0,
+                                bits, c->N, c->M, s));
+  else
+    LCP_RUN(launch_permute_f32((const float*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, PERM_FWD, (float*)D,
+                               bits, c->N, c->M, s));
+  tmr.stop(1);
+  tmr.start(2);
+  if (bf)
+    LCP_RUN(launch_gemm_error_bf16((const uint16_t*)D, L->cin, (const uint16_t*)L->X, L->cin, L->cout, L->T,
+                                   Ly.pitch, L->cin, (uint16_t*)R, Ly.pitch, part, s));
+  else
+    LCP_RUN(launch_gemm_error_f32((const float*)D, L->cin, (const float*)L->X, L->cin, L->cout, L->T, Ly.pitch,
+                                  L->cin, (float*)R, Ly.pitch, part, s));
+  tmr.stop(2);
+  tmr.start(3);
+  LCP_RUN(launch_error_finalize(part, Ly.nparts, Ews, err, s));
+  tmr.stop(3);
+  if (P_out)
+    LCP_RUN(hipMemcpyAsync(P_out, P, (size_t)Ly.nb * L->B * L->B * 4, hipMemcpyDeviceToDevice, s));
+  if (bits_out)
+    LCP_RUN(hipMemcpyAsync(bits_out, bits, (size_t)L->cout * (L->cin / 32) * 4, hipMemcpyDeviceToDevice, s));
+  return LCP_OK;
+}
+
+int lcp_step_bwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void* ws, size_t ws_bytes,
+                 float* dlogits, const lcp_timing* tm, void* stream) {
+  int rc = check_step_args(L, logits, c);
+  if (rc != LCP_OK) return rc;
+  if (!dlogits || !aligned16(dlogits)) return LCP_E_INVAL;
+  const bool bf = L->dtype == LCP_BF16;
+  if (bf && (!L->Xt || !aligned16(L->Xt))) return LCP_E_INVAL;
+  const StepLayout Ly = step_layout(L->cout, L->cin, L->T, L->B, c->iters, L->dtype);
+  rc = check_ws(ws, ws_bytes, Ly.total);
+  if (rc != LCP_OK) return rc;
+
+  char* base = (char*)ws;
+  const float* P = (const float*)(base + Ly.P);
+  const float* off = (const float*)(base + Ly.off);
+  const uint32_t* bits = (const uint32_t*)(base + Ly.bits);
+  void* Gd = base + Ly.D;           // G reuses the forward's D buffer
+  const void* R = base + Ly.R;
+  const float* Ews = (const float*)(base + Ly.E);
+  float* adj = (float*)(base + Ly.adj);
+  hipStream_t s = S(stream);
+  const Timer tmr{tm, s};
+
+  tmr.start(0);
+  if (bf)
+    LCP_RUN(launch_gemm_dd_bf16((const uint16_t*)R, Ly.pitch, (const uint16_t*)L->Xt, Ly.pitch, L->cout, L->cin,
+                                Ly.pitch, Ews, (uint16_t*)Gd, L->cin, s));
+  else
+    LCP_RUN(launch_gemm_dd_f32((const float*)R, Ly.pitch, (const float*)L->X, L->cin, L->cout, L->cin, L->T, Ews,
+                               (float*)Gd, L->cin, s));
+  tmr.stop(0);
+  tmr.start(1);
+  if (bf)
+    LCP_RUN(launch_adjoint_bf16((const uint16_t*)Gd, (const uint16_t*)L->W, P, bits, L->cout, L->cin, L->B,
+                                Ly.chunks, adj, s));
+  else
+    LCP_RUN(launch_adjoint_f32((const float*)Gd, (const float*)L->W, P, bits, L->cout, L->cin, L->B, Ly.chunks,
+                               adj, s));
+  tmr.stop(1);
+  tmr.start(2);
+  LCP_RUN(launch_sinkhorn_bwd(logits, adj, Ly.chunks, (size_t)Ly.nb * L->B * L->B, off, dlogits, Ly.nb, L->B,
+                              c->iters, c->tau, s));
+  tmr.stop(2);
+  return LCP_OK;
+}
+
+}  // extern "C"

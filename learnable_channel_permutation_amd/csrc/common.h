@@ -1,0 +1,78 @@
+// Device-side helpers shared by the gfx950 kernels of liblcp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- bfloat16 bit helpers -------------------------------------------------
+// float -> bf16 bits, round-to-nearest-even (inputs are finite or inf; a NaN
+// keeps a quiet NaN pattern).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 32x32x16 bf16 MFMA: acc[r] += sum_k A[l%32][k] B[k][l%32'] with lane l
+// holding A row (l%32), K slots 8*(l/32)+e and B column (l%32), K slots
+// 8*(l/32)+e; output register r of lane l is row 8*(r/4)+4*(l/32)+(r%4),
+// column l%32.
+__device__ __forceinline__ floatx16 mfma32(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Row remap used by the fused kernels: MFMA row rho = 8q + 4h + s (q < 4,
+// h < 2, s < 4) is given the logical index 16h + 4q + s, so that output
+// register r of a lane in half h holds logical row 16h + r (16 consecutive
+// rows per lane). remap_row(rho) maps rho -> logical; remap_inv the reverse.
+__device__ __host__ __forceinline__ int remap_row(int rho) {
+  return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
+}
+__device__ __host__ __forceinline__ int remap_inv(int k) {
+  return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3);
+}
+
+// ---- transcendental helpers (base 2, hardware v_exp_f32 / v_log_f32) --------
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---- N:M keep decision ------------------------------------------------------
+// Position k of a group is kept iff
+//   #{j: v_j > v_k} + #{j < k: v_j == v_k} < N
+// (ties to the lower position). NaN is read as -inf; IEEE compares treat
+// -0 == +0. Returns an M-bit mask, bit k = kept.
+__device__ __forceinline__ float nan_to_ninf(float v) { return (v != v) ? -__builtin_inff() : v; }
+
+template <int M>
+__device__ __forceinline__ uint32_t nm_keep(const float* v, int N) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < M; ++k) {
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      if (j == k) continue;
+      rank += (v[j] > v[k]) || (j < k && v[j] == v[k]);
+    }
+    bits |= (uint32_t)(rank < N) << k;
+  }
+  return bits;
+}
+
+// ---- wave helpers -------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace lcp

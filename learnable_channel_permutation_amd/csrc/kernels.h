@@ -1,0 +1,71 @@
+// Host-side launchers of the gfx950 kernels (internal to liblcp). Every
+// launcher enqueues on `s` and returns hipGetLastError() after the launch;
+// argument validation is done by the C ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcp {
+
+// Sinkhorn (sinkhorn.hip)
+hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb, int B,
+                               int iters, float tau, hipStream_t s);
+hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, int parts, size_t part_stride,
+                               const float* off, float* dlogits, int nb, int B, int iters,
+                               float tau, hipStream_t s);
+
+// Per-layer setup (layer.hip): column norms, optional bf16 transpose.
+hipError_t launch_colnorm_f32(const float* X, int T, int cin, float* norms, hipStream_t s);
+hipError_t launch_layer_init_bf16(const uint16_t* X, int T, int cin, int pitch, float* norms,
+                                  uint16_t* Xt, hipStream_t s);
+
+// N:M mask from fp32 scores (mask.hip).
+hipError_t launch_nm_mask(const float* scores, int rows, int cin, int N, int M, uint32_t* bits,
+                          hipStream_t s);
+
+// Block permutation kernels (permute.hip).
+enum PermMode {
+  PERM_PLAIN = 0,       // out = A P_B (or A P_B^T)
+  PERM_IMPORTANCE = 1,  // out = (|A| colscale) P_B, fp32, float32-accurate
+  PERM_FWD = 2          // D = W - ((W P_B) . M) P_B^T and mask bits from (|W| n) P_B
+};
+hipError_t launch_permute_bf16(const uint16_t* A, int rows, int cin, const float* colscale,
+                               const float* P, int B, int transposeP, int mode, void* out,
+                               int out_f32, uint32_t* bits, int N, int M, hipStream_t s);
+hipError_t launch_permute_f32(const float* A, int rows, int cin, const float* colscale,
+                              const float* P, int B, int transposeP, int mode, float* out,
+                              uint32_t* bits, int N, int M, hipStream_t s);
+hipError_t launch_diff(const void* W, const void* Wt, int n, int bf16, void* D, hipStream_t s);
+
+// GEMMs (gemm.hip). C[m][n] = sum_k A[m][k] B[n][k].
+// Error epilogue: store C (bf16 or f32, ldc) for n < n_store and write one
+// partial sum of squares per workgroup to part[]; returns the number of
+// partials through *nparts (host computed).
+int gemm_error_parts(int M, int N, int bf16);
+hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
+                                  int N_valid, int N_store, int K, uint16_t* C, int ldc,
+                                  float* part, hipStream_t s);
+hipError_t launch_gemm_error_f32(const float* A, int lda, const float* Bm, int ldb, int M,
+                                 int N_valid, int N_store, int K, float* C, int ldc, float* part,
+                                 hipStream_t s);
+// dD epilogue: C = -(1/E) * acc, with E read from device memory (0 -> 0).
+hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
+                               int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s);
+// f32 dD: C[m][n] = -(1/E) sum_t R[m][t] X[t][n]  (X row-major [K][N]).
+hipError_t launch_gemm_dd_f32(const float* R, int ldr, const float* X, int ldx, int M, int N,
+                              int K, const float* E, float* C, int ldc, hipStream_t s);
+hipError_t launch_error_finalize(const float* part, int nparts, float* E_ws, float* err,
+                                 hipStream_t s);
+
+// Block adjoint (adjoint.hip): partial dP over row chunks.
+int adjoint_chunks(int cout, int nb, int B);
+hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const float* P,
+                               const uint32_t* bits, int cout, int cin, int B, int chunks,
+                               float* part, hipStream_t s);
+hipError_t launch_adjoint_f32(const float* G, const float* W, const float* P,
+                              const uint32_t* bits, int cout, int cin, int B, int chunks,
+                              float* part, hipStream_t s);
+
+}  // namespace lcp

@@ -1,0 +1,153 @@
+"""Host-side contract of the C ABI (no GPU needed): the library loads, exports
+every function include/lcp.h declares, and rejects bad arguments with the
+documented status codes before touching the device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcp.h")
+
+
+def _lib():
+    from learnable_channel_permutation_amd import _lib as L
+    return L
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcp_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_step_entry_points():
+    names = _declared()
+    for n in ("lcp_sinkhorn", "lcp_permute", "lcp_nm_mask", "lcp_error", "lcp_step_fwd", "lcp_step_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    lib = ctypes.CDLL(L._LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert sorted(L.EXPORTS) == _declared()
+
+
+def test_status_strings_and_version():
+    L = _lib()
+    assert L.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert L.status_string(code) not in ("ok", "unknown status")
+    assert L.status_string(12345) == "unknown status"
+    assert L.LIB.lcp_version() >= 100
+
+
+def test_xt_pitch():
+    L = _lib()
+    assert L.lcp_xt_pitch(1) == 64
+    assert L.lcp_xt_pitch(64) == 64
+    assert L.lcp_xt_pitch(2048) == 2048
+    assert L.lcp_xt_pitch(2049) == 2112
+    assert L.lcp_xt_pitch(0) == -1
+
+
+def test_workspace_queries():
+    L = _lib()
+    a = L.lcp_step_workspace_bytes(4096, 11008, 2048, 64, 5, L.LCP_BF16)
+    # P + offsets + bits + D + R at least
+    floor = 172 * 64 * 64 * 4 + 172 * 5 * 2 * 64 * 4 + 4096 * 344 * 4 + 4096 * 11008 * 2 + 4096 * 2048 * 2
+    assert a >= floor and a % 256 == 0
+    b = L.lcp_step_workspace_bytes(4096, 11008, 2048, 64, 5, L.LCP_F32)
+    assert b > a
+    with pytest.raises(L.LcpError) as e:
+        L.lcp_step_workspace_bytes(4096, 11000, 2048, 64, 5, L.LCP_BF16)   # cin % B
+    assert e.value.code == L.LCP_E_INVAL
+    with pytest.raises(L.LcpError) as e:
+        L.lcp_step_workspace_bytes(4096, 11008, 2048, 16 * 43, 5, L.LCP_BF16)   # B unsupported
+    assert e.value.code in (L.LCP_E_UNSUPPORTED, L.LCP_E_INVAL)
+    assert L.lcp_error_workspace_bytes(256, 256, 256, L.LCP_F32) > 256 * 256 * 4
+
+
+def _fake(addr=0x100000):
+    return ctypes.c_void_p(addr)
+
+
+def test_invalid_arguments_return_codes_without_launching():
+    """Every call below fails validation, so no HIP call is made (this runs
+    on a machine without a GPU)."""
+    L = _lib()
+    lib = L.LIB
+    p = _fake()
+    s = None
+    # sinkhorn
+    assert lib.lcp_sinkhorn(None, p, 4, 64, 5, 1.0, s) == L.LCP_E_INVAL
+    assert lib.lcp_sinkhorn(p, p, 4, 64, 0, 1.0, s) == L.LCP_E_INVAL
+    assert lib.lcp_sinkhorn(p, p, 4, 64, 5, 0.0, s) == L.LCP_E_INVAL
+    assert lib.lcp_sinkhorn(p, p, 4, 64, 5, -1.0, s) == L.LCP_E_INVAL
+    assert lib.lcp_sinkhorn(p, p, 4, 64, 5, math.inf, s) == L.LCP_E_INVAL
+    assert lib.lcp_sinkhorn(p, p, 4, 64, 5, math.nan, s) == L.LCP_E_INVAL
+    assert lib.lcp_sinkhorn(p, p, 4, 48, 5, 1.0, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_sinkhorn(p, p, 4, 64, 1000, 1.0, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_sinkhorn(_fake(0x100004), p, 4, 64, 5, 1.0, s) == L.LCP_E_INVAL  # misaligned
+    assert lib.lcp_sinkhorn_bwd(p, p, 4, 64, 5, 1.0, p, s) == L.LCP_E_INVAL        # dlogits aliases dP
+    # mask
+    assert lib.lcp_nm_mask(p, 8, 64, 0, 4, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_nm_mask(p, 8, 64, 4, 4, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_nm_mask(p, 8, 48, 2, 4, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_nm_mask(p, 8, 64, 2, 16, p, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_nm_mask(p, 0, 64, 2, 4, p, s) == L.LCP_E_INVAL
+    # permute
+    assert lib.lcp_permute(p, L.LCP_BF16, 8, 100, None, p, 64, 0, p, L.LCP_BF16, s) == L.LCP_E_INVAL
+    assert lib.lcp_permute(p, L.LCP_BF16, 8, 96, None, p, 96, 0, p, L.LCP_BF16, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_permute(p, L.LCP_BF16, 8, 128, p, p, 64, 0, p, L.LCP_BF16, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_permute(p, 7, 8, 128, None, p, 64, 0, p, L.LCP_BF16, s) == L.LCP_E_UNSUPPORTED
+    # colnorm / layer init
+    assert lib.lcp_colnorm(p, L.LCP_BF16, 0, 64, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_layer_init(p, L.LCP_BF16, 16, 64, p, None, s) == L.LCP_E_INVAL    # bf16 needs Xt
+    assert lib.lcp_layer_init(p, L.LCP_BF16, 16, 48, p, p, s) == L.LCP_E_INVAL      # cin % 32
+    # error
+    n = ctypes.c_size_t(1 << 20)
+    assert lib.lcp_error(p, p, p, L.LCP_BF16, 8, 64, 16, None, None, p, n, s) == L.LCP_E_INVAL
+    assert lib.lcp_error(p, p, p, L.LCP_BF16, 8, 64, 16, p, None, p, ctypes.c_size_t(16), s) == L.LCP_E_WORKSPACE
+    assert lib.lcp_error(p, p, p, L.LCP_BF16, 8, 64, 16, p, None, _fake(0x100010), n, s) == L.LCP_E_WORKSPACE
+
+
+def test_step_argument_validation():
+    L = _lib()
+    lib = L.LIB
+    p = 0x100000
+    layer = L.lcp_layer(p, p, p, p, L.LCP_BF16, 64, 128, 32, 64)
+    cfg = L.lcp_cfg(5, 1.0, 2, 4)
+    ws = ctypes.c_void_p(p)
+    need = L.lcp_step_workspace_bytes(64, 128, 32, 64, 5, L.LCP_BF16)
+    err = ctypes.c_void_p(p)
+
+    def fwd(layer=layer, cfg=cfg, ws=ws, n=need, err=err):
+        return lib.lcp_step_fwd(ctypes.byref(layer), ctypes.c_void_p(p), ctypes.byref(cfg), ws,
+                                ctypes.c_size_t(n), err, None, None, None, None)
+
+    def bwd(layer=layer, cfg=cfg, ws=ws, n=need):
+        return lib.lcp_step_bwd(ctypes.byref(layer), ctypes.c_void_p(p), ctypes.byref(cfg), ws,
+                                ctypes.c_size_t(n), ctypes.c_void_p(p), None, None)
+
+    assert fwd(n=need - 1) == L.LCP_E_WORKSPACE
+    assert fwd(ws=ctypes.c_void_p(p + 128)) == L.LCP_E_WORKSPACE
+    assert fwd(err=None) == L.LCP_E_INVAL
+    assert fwd(cfg=L.lcp_cfg(0, 1.0, 2, 4)) == L.LCP_E_INVAL
+    assert fwd(cfg=L.lcp_cfg(5, 0.0, 2, 4)) == L.LCP_E_INVAL
+    assert fwd(cfg=L.lcp_cfg(5, 1.0, 4, 4)) == L.LCP_E_INVAL
+    assert fwd(cfg=L.lcp_cfg(5, 1.0, 0, 4)) == L.LCP_E_INVAL
+    assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 16)) in (L.LCP_E_UNSUPPORTED, L.LCP_E_INVAL)
+    assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 3)) == L.LCP_E_INVAL           # B % M
+    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 64, 96, 32, 64)) == L.LCP_E_INVAL   # cin % B
+    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 64, 96, 32, 96)) == L.LCP_E_UNSUPPORTED
+    assert fwd(layer=L.lcp_layer(p, p, p, p, 5, 64, 128, 32, 64)) == L.LCP_E_UNSUPPORTED
+    assert fwd(layer=L.lcp_layer(0, p, p, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL
+    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 0, 128, 32, 64)) == L.LCP_E_INVAL
+    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 1 << 20, 1 << 12, 32, 64)) == L.LCP_E_INVAL
+    assert bwd(layer=L.lcp_layer(p, p, 0, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL   # bf16 needs Xt
+    assert bwd(n=need - 256) == L.LCP_E_WORKSPACE

@@ -1,0 +1,320 @@
+"""GPU parity: every kernel of the LCP step against the float64 oracle, through
+the C ABI, on seeded inputs. Tolerances: Sinkhorn per entry 1e-5 relative +
+1e-9; masks bit-exact on the oracle's scores and >= 99.9 % of bits end to end;
+GEMM residual and error 1e-2 relative; gradients 2e-2 relative (Frobenius)."""
+import numpy as np
+import pytest
+import torch
+
+import lcp_synth
+import oracle
+from tests.gpu_util import DEV, bit_agreement, bits_down, down, empty_bits, rel_fro, say, up
+
+pytestmark = pytest.mark.gpu
+
+lcp = pytest.importorskip("learnable_channel_permutation_amd")
+L = lcp._lib
+
+
+def _sink_tol(ref):
+    return 1e-5 * np.abs(ref) + 1e-9
+
+
+# ------------------------------------------------------------------ Sinkhorn --
+@pytest.mark.parametrize("B,iters,tau,kind", [
+    (32, 5, 1.0, "eye"), (64, 5, 1.0, "eye"), (128, 7, 1.0, "eye"),
+    (32, 1, 1.0, "randn"), (64, 5, 0.5, "randn"), (128, 5, 1.0, "randn"),
+    (64, 20, 1.0, "randn"), (64, 5, 0.1, "eye"), (32, 3, 2.0, "uniform"),
+])
+def test_sinkhorn_forward(B, iters, tau, kind):
+    nb = 37
+    if kind == "eye":
+        lg = lcp_synth.make_logits(np.random.Generator(np.random.PCG64(B + iters)), nb, B)
+    elif kind == "randn":
+        lg = lcp_synth.random_logits(B * 7 + iters, nb, B)
+    else:
+        lg = np.full((nb, B, B), 0.25, dtype=np.float32)
+    say("sinkhorn fwd", B, iters, tau, kind)
+    d_lg = up(lg)
+    d_P = torch.empty_like(d_lg)
+    L.lcp_sinkhorn(d_lg, d_P, iters, tau)
+    torch.cuda.synchronize()
+    ref = oracle.sinkhorn(lg.astype(np.float64), np.float64(np.float32(tau)), iters)
+    got = down(d_P)
+    assert np.all(np.abs(got - ref) <= _sink_tol(ref)), np.max(np.abs(got - ref) / (np.abs(ref) + 1e-9))
+    # in place
+    L.lcp_sinkhorn(d_lg, d_lg, iters, tau)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(d_lg), got)
+
+
+@pytest.mark.parametrize("B,iters,tau", [(32, 5, 1.0), (64, 5, 0.7), (128, 7, 1.0), (64, 1, 1.0)])
+def test_sinkhorn_backward(B, iters, tau):
+    nb = 19
+    lg = lcp_synth.random_logits(100 + B, nb, B, scale=0.5)
+    dP = lcp_synth.random_matrix(200 + B, (nb, B, B))
+    say("sinkhorn bwd", B, iters, tau)
+    d_out = torch.empty((nb, B, B), dtype=torch.float32, device=DEV)
+    L.lcp_sinkhorn_bwd(up(lg), up(dP), iters, tau, d_out)
+    torch.cuda.synchronize()
+    tau64 = np.float64(np.float32(tau))
+    P, tr = oracle.sinkhorn(lg.astype(np.float64), tau64, iters, trace=True)
+    ref = oracle.sinkhorn_adjoint(dP.astype(np.float64), P, tr, tau64)
+    assert rel_fro(down(d_out), ref) < 1e-4
+
+
+# ---------------------------------------------------------------- N:M mask --
+def _mask_scores(rows, cin, seed):
+    lay = lcp_synth.make_layer(lcp_synth.CONFIGS[2], seed=seed, cout=rows, cin=cin, T=64)
+    fw = oracle.step_forward(lay.W, lay.X, lay.logits, 1.0, 5, 2, 4)
+    S = fw["S_hat"].astype(np.float32)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S[0, :] = 1.0                                          # all ties
+    S[1, :] = rng.integers(0, 3, size=cin).astype(np.float32)  # many ties
+    S[2, ::5] = np.nan
+    S[3, ::7] = np.inf
+    S[3, 1::7] = -np.inf
+    S[4, ::2] = -0.0
+    S[4, 1::2] = 0.0
+    return S
+
+
+@pytest.mark.parametrize("N,M", [(1, 4), (2, 4), (3, 4), (1, 8), (2, 8), (4, 8), (7, 8)])
+def test_nm_mask_bit_exact(N, M):
+    rows, cin = 67, 256
+    S = _mask_scores(rows, cin, 31 + N + M)
+    say("nm_mask", N, M)
+    bits = empty_bits(rows, cin)
+    L.lcp_nm_mask(up(S), N, M, bits)
+    torch.cuda.synchronize()
+    want = oracle.pack_bits(oracle.nm_mask(S, N, M))
+    got = bits_down(bits)
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------ layer setup --
+@pytest.mark.parametrize("T,cin", [(100, 96), (2048, 256), (64, 32)])
+def test_layer_init_bf16(T, cin):
+    lay = lcp_synth.make_layer(lcp_synth.CONFIGS[0], seed=5, cout=32, cin=cin, T=T, dtype="bf16")
+    say("layer_init bf16", T, cin)
+    X = up(lay.X, torch.bfloat16)
+    norms = torch.empty(cin, dtype=torch.float32, device=DEV)
+    pitch = L.lcp_xt_pitch(T)
+    Xt = torch.full((cin, pitch), 7.0, dtype=torch.bfloat16, device=DEV)
+    L.lcp_layer_init(X, norms, Xt)
+    n2 = torch.empty_like(norms)
+    L.lcp_colnorm(X, n2)
+    torch.cuda.synchronize()
+    ref = oracle.colnorm(lay.X)
+    assert np.max(np.abs(down(norms) - ref) / ref) < 1e-5
+    assert np.array_equal(down(norms), down(n2))
+    xt = down(Xt)
+    assert np.array_equal(xt[:, :T], lay.X.T.astype(np.float64))
+    assert np.all(xt[:, T:] == 0)
+
+
+def test_colnorm_f32():
+    lay = lcp_synth.make_layer(lcp_synth.CONFIGS[0], seed=6, cout=32, cin=96, T=77)
+    say("colnorm f32")
+    norms = torch.empty(96, dtype=torch.float32, device=DEV)
+    L.lcp_colnorm(up(lay.X), norms)
+    torch.cuda.synchronize()
+    ref = oracle.colnorm(lay.X)
+    assert np.max(np.abs(down(norms) - ref) / ref) < 1e-5
+
+
+# ------------------------------------------------------------------ permute --
+def _perm_case(rows, cin, B, seed, dtype="bf16"):
+    W = lcp_synth.random_matrix(seed, (rows, cin), std=0.02, dtype=dtype)
+    lg = lcp_synth.random_logits(seed + 1, cin // B, B, scale=1.0)
+    P = oracle.sinkhorn(lg.astype(np.float64), 1.0, 5).astype(np.float32)
+    return W, P
+
+
+@pytest.mark.parametrize("rows,cin,B", [(100, 192, 64), (300, 256, 128), (77, 96, 32), (256, 512, 64)])
+@pytest.mark.parametrize("transposeP", [False, True])
+def test_permute_plain_bf16(rows, cin, B, transposeP):
+    W, P = _perm_case(rows, cin, B, rows + cin + B)
+    say("permute plain bf16", rows, cin, B, transposeP)
+    dW = up(W, torch.bfloat16)
+    out32 = torch.empty((rows, cin), dtype=torch.float32, device=DEV)
+    out16 = torch.empty((rows, cin), dtype=torch.bfloat16, device=DEV)
+    L.lcp_permute(dW, up(P), B, out32, transposeP=transposeP)
+    L.lcp_permute(dW, up(P), B, out16, transposeP=transposeP)
+    torch.cuda.synchronize()
+    ref = oracle.block_permute(W, P, transpose=transposeP)
+    # P enters the MFMA as bf16 (relative rounding <= 2^-9 per entry), products
+    # are exact and accumulate in fp32; bf16 output adds 2^-9 relative.
+    bound = oracle.block_permute(np.abs(W), np.abs(P), transpose=transposeP) * 2.0 ** -8 + 1e-12
+    assert np.all(np.abs(down(out32) - ref) <= bound)
+    assert np.all(np.abs(down(out16) - ref) <= bound + np.abs(ref) * 2.0 ** -8)
+
+
+@pytest.mark.parametrize("rows,cin,B", [(100, 192, 64), (300, 256, 128), (77, 96, 32)])
+def test_permute_importance_bf16(rows, cin, B):
+    W, P = _perm_case(rows, cin, B, 3 * rows + B)
+    n = (np.random.Generator(np.random.PCG64(rows)).lognormal(0, 1, cin) * 40).astype(np.float32)
+    say("permute importance bf16", rows, cin, B)
+    out = torch.empty((rows, cin), dtype=torch.float32, device=DEV)
+    L.lcp_permute(up(W, torch.bfloat16), up(P), B, out, colscale=up(n))
+    torch.cuda.synchronize()
+    ref = oracle.block_permute(oracle.importance(W, n), P)
+    # float32-accurate: n_j P_jk rounds once to fp32, its bf16 split is exact
+    # (B = 128 keeps two terms: 2^-17), products exact, fp32 accumulation
+    rel = np.abs(down(out) - ref) / np.maximum(ref, 1e-30)
+    assert np.max(rel) < (2e-5 if B == 128 else 5e-6), np.max(rel)
+
+
+@pytest.mark.parametrize("B", [32, 64, 128])
+def test_permute_f32(B):
+    rows, cin = 45, 2 * B
+    W, P = _perm_case(rows, cin, B, 11 * B, dtype="f32")
+    n = np.abs(lcp_synth.random_matrix(5, (cin,))) + 0.5
+    say("permute f32", B)
+    out = torch.empty((rows, cin), dtype=torch.float32, device=DEV)
+    L.lcp_permute(up(W), up(P), B, out)
+    imp = torch.empty_like(out)
+    L.lcp_permute(up(W), up(P), B, imp, colscale=up(n))
+    torch.cuda.synchronize()
+    assert rel_fro(down(out), oracle.block_permute(W, P)) < 1e-6
+    assert rel_fro(down(imp), oracle.block_permute(oracle.importance(W, n), P)) < 1e-6
+
+
+# -------------------------------------------------------------------- error --
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("cout,cin,T", [(300, 352, 200), (256, 256, 256), (513, 128, 65)])
+def test_error_gemm(dtype, cout, cin, T):
+    W = lcp_synth.random_matrix(1 + cout, (cout, cin), std=0.02, dtype=dtype)
+    Wt = lcp_synth.random_matrix(2 + cout, (cout, cin), std=0.02, dtype=dtype)
+    X = lcp_synth.random_matrix(3 + cout, (T, cin), std=1.0, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    say("error gemm", dtype, cout, cin, T)
+    ws = torch.empty(L.lcp_error_workspace_bytes(cout, cin, T, L.LCP_BF16 if dtype == "bf16" else L.LCP_F32),
+                     dtype=torch.uint8, device=DEV)
+    err = torch.empty(1, dtype=torch.float32, device=DEV)
+    pitch = L.lcp_xt_pitch(T)
+    R = torch.full((cout, pitch), 3.0, dtype=tdt, device=DEV)
+    L.lcp_error(up(W, tdt), up(Wt, tdt), up(X, tdt), err, ws, R_out=R)
+    torch.cuda.synchronize()
+    Rref, Eref = oracle.pruning_error(W.astype(np.float64) - Wt, X)
+    Rg = down(R)
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    assert abs(float(err.item()) - Eref) / Eref < tol
+    assert rel_fro(Rg[:, :T], Rref) < tol
+    assert np.all(Rg[:, T:] == 0)
+
+
+# --------------------------------------------------------------- full step --
+def _run_step(lay, spec, backward=True, dtype=None):
+    dtype = dtype or spec.dtype
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    W, X = up(lay.W, tdt), up(lay.X, tdt)
+    lg = up(lay.logits)
+    s = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, spec.N, spec.M)
+    P = torch.empty_like(lg)
+    bits = empty_bits(lay.cout, lay.cin)
+    err = s.forward(lg, P_out=P, bits_out=bits)
+    dl = s.backward(lg) if backward else None
+    torch.cuda.synchronize()
+    return float(err.item()), down(P), bits_down(bits), (down(dl) if dl is not None else None)
+
+
+def _check_step(lay, spec, got, backward=True, e_tol=1e-2):
+    E, P, bits, dl = got
+    fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M)
+    assert np.all(np.abs(P - fw["P"]) <= _sink_tol(fw["P"]))
+    agree = bit_agreement(bits, oracle.pack_bits(fw["mask"]), lay.cout * lay.cin)
+    assert agree >= 0.999, agree
+    assert abs(E - fw["E"]) / fw["E"] < e_tol, (E, fw["E"])
+    if backward:
+        bw = oracle.step_backward(fw, lay.X, lay.W)
+        r = rel_fro(dl, bw["dlogits"])
+        assert r < 2e-2, r
+    return fw
+
+
+SMALL = [
+    # (config index, cout, cin, T): shapes with several tiles and ragged tails
+    (1, 300, 512, 200),
+    (2, 520, 640, 130),
+    (3, 270, 512, 160),
+    (4, 257, 384, 96),
+    (2, 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("ci,cout,cin,T", SMALL)
+def test_step_small(ci, cout, cin, T):
+    spec = lcp_synth.CONFIGS[ci]
+    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
+    say("step", spec.name, cout, cin, T)
+    got = _run_step(lay, spec)
+    _check_step(lay, spec, got)
+
+
+def test_step_c1_fp32_full_size():
+    """The 256 x 256 float32 layer at its full size, forward and backward."""
+    spec = lcp_synth.CONFIGS[0]
+    lay = lcp_synth.make_layer(spec)
+    say("step C1 f32 full")
+    got = _run_step(lay, spec, backward=True)
+    _check_step(lay, spec, got, backward=True, e_tol=1e-4)
+
+
+def test_step_random_logits_and_harder_tau():
+    spec = lcp_synth.CONFIGS[2]
+    lay = lcp_synth.make_layer(spec, cout=200, cin=256, T=100)
+    lay.logits[:] = lcp_synth.random_logits(77, 4, 64, scale=1.0)
+    spec2 = lcp_synth.LayerSpec(**{**spec.__dict__, "tau": 0.5, "iters": 7})
+    say("step random logits tau 0.5")
+    got = _run_step(lay, spec2)
+    _check_step(lay, spec2, got)
+
+
+def test_step_zero_error_gives_zero_gradient():
+    spec = lcp_synth.CONFIGS[2]
+    lay = lcp_synth.make_layer(spec, cout=64, cin=128, T=64)
+    lay.X[:] = 0.0
+    say("step zero X")
+    E, P, bits, dl = _run_step(lay, spec)
+    assert E == 0.0
+    assert np.all(dl == 0.0)
+
+
+def test_step_peaked_logits_is_hard_pruning():
+    """Sharply peaked logits make P a hard permutation: D = W with the pruned
+    entries only, so E equals the error of plain N:M pruning of the gathered
+    channels (oracle with the hard P)."""
+    spec = lcp_synth.CONFIGS[2]
+    lay = lcp_synth.make_layer(spec, cout=128, cin=128, T=64)
+    rng = np.random.Generator(np.random.PCG64(9))
+    Pi = np.zeros((2, 64, 64))
+    for b in range(2):
+        Pi[b, rng.permutation(64), np.arange(64)] = 1.0
+    lay.logits[:] = (60.0 * Pi).astype(np.float32)
+    say("step peaked logits")
+    E, P, bits, dl = _run_step(lay, spec, backward=False)
+    fw = oracle.step_forward(lay.W, lay.X, None, 1.0, 1, 2, 4, P=Pi)
+    assert abs(E - fw["E"]) / fw["E"] < 1e-2
+    assert bit_agreement(bits, oracle.pack_bits(fw["mask"]), 128 * 128) == 1.0
+
+
+def test_step_deterministic():
+    spec = lcp_synth.CONFIGS[2]
+    lay = lcp_synth.make_layer(spec, cout=384, cin=256, T=128)
+    say("step determinism")
+    a = _run_step(lay, spec)
+    b = _run_step(lay, spec)
+    assert a[0] == b[0]
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+
+
+def test_step_full_size_bench_layer():
+    """The 4096 x 11008 layer at full size, in the launch configuration the
+    benchmark times: P, every mask bit, E and the gradient against the full
+    float64 oracle."""
+    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    lay = lcp_synth.make_layer(spec)
+    say("step full size", spec.name)
+    got = _run_step(lay, spec)
+    _check_step(lay, spec, got)
