@@ -1,0 +1,260 @@
+"""Benchmark: LCP forward + backward steps per second on one linear layer.
+
+Workload: the LLaMA-7B down_proj-shaped layer, W 4096 x 11008 bf16, X 2048
+tokens x 11008 bf16 with lognormal channel scales, block size 64, 5 Sinkhorn
+iterations at tau = 1, 2:4 mask; seeded synthetic data (no model weights or
+calibration text exist here).
+
+One step = the whole hot path: per-layer setup (column norms, X transposed),
+Sinkhorn, fused permute / importance / mask / un-permute, error GEMM and its
+norm, backward GEMM, block adjoint and Sinkhorn adjoint, all in liblcp.so.
+Inputs are resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--breakdown]
+
+Prints one JSON line. `roofline` is computed from the average duration of the
+dominant kernel, measured with HIP events recorded on the step's stream inside
+the timed region; `cpu_baseline` times the float64 oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+FWD_NAMES = ["sinkhorn_fwd", "permute_mask_unpermute", "error_gemm", "error_finalize"]
+BWD_NAMES = ["dD_gemm", "block_adjoint", "sinkhorn_bwd"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=None, help="layer config index (default: the bench layer)")
+    ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies of MIB MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "learnable_channel_permutation_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+class HipEvents:
+    """hipEvent_t handles created and read through the HIP runtime (the library
+    records them on the step's stream; torch's Event wrapper only accepts
+    events it recorded itself)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(e)
+        return e
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+
+class _Ev:
+    """Adapter so make_timing() can take raw hipEvent_t handles."""
+
+    def __init__(self, h):
+        self.cuda_event = h.value
+
+
+def cpu_baseline(spec, lay):
+    """The float64 oracle, untuned, for one full forward + backward step of the
+    same layer on the host cores (one step is the sample)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M)
+    oracle.step_backward(fw, lay.X, lay.W)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": "one full forward+backward step of the same %dx%d layer (T=%d), float64 NumPy, %.1f s"
+                      % (spec.cout, spec.cin, spec.T, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lcp_synth
+    import learnable_channel_permutation_amd as lcp
+
+    if args.copy_probe > 0:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ci = lcp_synth.BENCH_CONFIG if args.config is None else args.config
+    spec = lcp_synth.CONFIGS[ci]
+    lay = lcp_synth.make_layer(spec)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    W = torch.from_numpy(lay.W).to(dev).to(tdt)
+    X = torch.from_numpy(lay.X).to(dev).to(tdt)
+    logits = torch.from_numpy(lay.logits).to(dev)
+    dlogits = torch.empty_like(logits)
+    sess = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, spec.N, spec.M)
+    stream = torch.cuda.current_stream()
+
+    def step(tf=None, tb=None):
+        sess.init()
+        sess.forward(logits, timing=tf)
+        if spec.backward:
+            sess.backward(logits, dlogits, timing=tb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, plus events around the two GEMMs on the same stream
+    K = args.steps
+    he = HipEvents()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    g_fwd = [(he.new(), he.new()) for _ in range(K)]
+    g_bwd = [(he.new(), he.new()) for _ in range(K)]
+    tfs = [lcp.make_timing([None, None, _Ev(a)], [None, None, _Ev(b)]) for a, b in g_fwd]
+    tbs = [lcp.make_timing([_Ev(a)], [_Ev(b)]) for a, b in g_bwd]
+    t_start, t_stop = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(K):
+        step(tfs[k], tbs[k] if spec.backward else None)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_stop) / K
+    fwd_gemm_ms = sum(he.ms(a, b) for a, b in g_fwd) / K
+    bwd_gemm_ms = sum(he.ms(a, b) for a, b in g_bwd) / K if spec.backward else 0.0
+
+    flops_gemm = 2.0 * spec.cout * spec.cin * spec.T
+    dom_name, dom_ms = ("error_gemm", fwd_gemm_ms)
+    if bwd_gemm_ms > fwd_gemm_ms:
+        dom_name, dom_ms = ("dD_gemm", bwd_gemm_ms)
+    achieved = flops_gemm / (dom_ms * 1e-3) / 1e12
+    traffic = measured_traffic(dom_name)
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
+            "kernel_ms": round(dom_ms, 4),
+            "other_gemm": {"kernel": "dD_gemm" if dom_name == "error_gemm" else "error_gemm",
+                           "ms": round(bwd_gemm_ms if dom_name == "error_gemm" else fwd_gemm_ms, 4)}}
+
+    if args.breakdown:
+        names = FWD_NAMES + (BWD_NAMES if spec.backward else [])
+        reps = 20
+        evs = {n: [(he.new(), he.new()) for _ in range(reps)] for n in names}
+        init_ev = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for r in range(reps):
+            init_ev[r][0].record(stream)
+            sess.init()
+            init_ev[r][1].record(stream)
+            tf = lcp.make_timing([_Ev(evs[n][r][0]) for n in FWD_NAMES], [_Ev(evs[n][r][1]) for n in FWD_NAMES])
+            sess.forward(logits, timing=tf)
+            if spec.backward:
+                tb = lcp.make_timing([_Ev(evs[n][r][0]) for n in BWD_NAMES],
+                                     [_Ev(evs[n][r][1]) for n in BWD_NAMES])
+                sess.backward(logits, dlogits, timing=tb)
+        torch.cuda.synchronize()
+        print("per-kernel ms (mean of %d):" % reps, file=sys.stderr)
+        print("  %-24s %8.4f" % ("layer_init", sum(a.elapsed_time(b) for a, b in init_ev) / reps), file=sys.stderr)
+        for n in names:
+            print("  %-24s %8.4f" % (n, sum(he.ms(a, b) for a, b in evs[n]) / reps), file=sys.stderr)
+    he.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, lay)
+
+    out = {
+        "metric": "LCP fwd+bwd steps/sec per layer (4096x11008, 2:4)",
+        "value": round(1000.0 / ms, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded LLaMA-shaped layer; no weights or calibration text available)",
+        "config": {"workload": "lcp_step_fwd_bwd", "layer": spec.name, "cout": spec.cout, "cin": spec.cin,
+                   "T": spec.T, "B": spec.B, "sinkhorn_iters": spec.iters, "tau": spec.tau,
+                   "N": spec.N, "M": spec.M, "backward": spec.backward,
+                   "includes_layer_setup": True},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
