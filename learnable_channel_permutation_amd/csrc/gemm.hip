@@ -3,17 +3,24 @@
 // with A and B row-major and K contiguous (the backward reads X transposed,
 // prepared once per layer).
 //
-// bf16 kernel (gfx950): 256 x 128 x 64 tiles, 4 waves in a 2 x 2 layout, each
-// wave 128 x 64 = 4 x 2 MFMA 32x32x16 blocks with fp32 accumulators. Global
-// tiles are loaded as 16-byte chunks into registers and stored to LDS
-// (double-buffered, one barrier per K step); chunk c of row r sits at
-// position c ^ (r & 7) so the 16-byte fragment reads of 8 consecutive rows hit
-// distinct banks. The MFMA A operand is taken from the B matrix with the row
-// remap of common.h, so each lane ends up holding 16 consecutive output
-// columns of one output row and writes them as two 16-byte stores.
-// Workgroups are ordered so that each XCD (workgroup id mod 8) works on a
-// compact group of 4 row panels x 8 column panels, which keeps the panels
-// shared inside that XCD's L2.
+// bf16 kernel (gfx950): BM x BN x 64 tiles, 8 waves (two per SIMD) in a
+// 4 x 2 layout, each wave owning (BM/4) x (BN/2) of the tile as MFMA 32x32x16
+// blocks with fp32 accumulators. Operand tiles move global -> LDS with
+// 16-byte direct-to-LDS loads (no register staging) into a two-stage ring;
+// one barrier per K step, and the next tile's loads are in flight while the
+// current one is multiplied. Chunk c of row r is stored at position
+// c ^ ((r >> 1) & 7): the 16-byte fragment reads of 16 consecutive rows then
+// cover all 64 LDS banks. Inside a K step the MFMAs of one 16-wide sub-step
+// are interleaved one-to-one with the fragment reads of the next
+// (sched_group_barrier), so LDS latency hides under MFMA work. The MFMA A
+// operand is taken from the B matrix with the row remap of common.h, so each
+// lane ends up holding 16 consecutive output columns of one output row and
+// writes them as two 16-byte stores. Workgroups are ordered so that each XCD
+// (workgroup id mod 8) works on a compact group of 4 row panels x N column
+// panels, which keeps the panels shared inside that XCD's L2.
+// Out-of-range rows are read from a clamped row (their outputs are never
+// stored); out-of-range K chunks and B rows read a 16-byte zero block, so
+// padded output columns come out exactly zero.
 //
 // Epilogues: ERR stores C in bf16 and one sum of squares of the fp32
 // accumulators per workgroup (reduced later in a fixed order); DD scales by
@@ -25,8 +32,12 @@ namespace lcp {
 
 enum { EPI_ERR = 0, EPI_DD = 1 };
 
-constexpr int GBM = 256, GBN = 128, GBK = 64;
+constexpr int GBK = 64;
 constexpr int GROUP_M = 4;
+constexpr int GWM = 4, GWN = 2, GNW = GWM * GWN, GNT = 64 * GNW;   // wave layout, threads
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ const u32x4 g_zero16[1] = {{0u, 0u, 0u, 0u}};
 
 __device__ __forceinline__ void tile_coords(int g, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
   int logical = g;
@@ -40,54 +51,67 @@ __device__ __forceinline__ void tile_coords(int g, int G, int tiles_m, int tiles
   tn = rem / gsm;
 }
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ (row & 7)) << 3); }
+__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 1) & 7)) << 3); }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
+// Pin the order of one K step: the first sub-step's fragment reads, then for
+// every sub-step its MFMAs interleaved with the next sub-step's reads.
+template <int FM, int FN>
+__device__ __forceinline__ void pin_schedule() {
+  constexpr int NR = FM + FN, NM = FM * FN;
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+  for (int p = 0; p < GBK / 16; ++p) {
+    if (p + 1 < GBK / 16) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    }
+  }
+}
+
+template <int BM, int BN>
+constexpr size_t gemm_lds_bytes() { return (size_t)2 * (BM + BN) * GBK * 2; }
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M,
     int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, float* __restrict__ part,
     const float* __restrict__ Eptr) {
-  constexpr int WM = GBM / 2, WN = GBN / 2;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int ACH = GBM * 8 / 256, BCH = GBN * 8 / 256;   // 16-byte chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * GBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GBN * GBK];
+  constexpr int WM = BM / GWM, WN = BN / GWN, FM = WM / 32, FN = WN / 32;
+  constexpr int AI = BM * 8 / GNT, BI = BN * 8 / GNT;     // 16-byte loads per thread per tile
+  constexpr int STAGE = (BM + BN) * GBK;                   // bf16 elements per ring stage
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
-  const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N_store + GBN - 1) / GBN;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N_store + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * GBM, n0 = tn * GBN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / GWN, wn = w % GWN;
   const int h = l >> 5, ln = l & 31;
 
-  u32x4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) {
+  // load instruction q of wave w fills the 64 consecutive 16-byte chunks
+  // (q * GNW + w) * 64 + lane of the stage
+  auto issue = [&](int stage, int k0) {
+    uint16_t* sb = lds + stage * STAGE;
 #pragma unroll
-    for (int q = 0; q < ACH; ++q) {
-      const int id = t + 256 * q, row = id >> 3, ch = id & 7;
-      const int gm = m0 + row, gk = k0 + ch * 8;
-      ra[q] = (gm < M && gk < K) ? *reinterpret_cast<const u32x4*>(A + (size_t)gm * lda + gk)
-                                 : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < AI; ++q) {
+      const int c = (q * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+      const int gm = min(m0 + row, M - 1), gk = k0 + ch * 8;
+      const void* src = (gk < K) ? (const void*)(A + (size_t)gm * lda + gk) : (const void*)g_zero16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + (q * GNW + w) * 64 * 8), 16, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < BCH; ++q) {
-      const int id = t + 256 * q, row = id >> 3, ch = id & 7;
+    for (int q = 0; q < BI; ++q) {
+      const int c = (q * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
       const int gn = n0 + row, gk = k0 + ch * 8;
-      rb[q] = (gn < N_valid && gk < K) ? *reinterpret_cast<const u32x4*>(Bm + (size_t)gn * ldb + gk)
-                                       : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < ACH; ++q) {
-      const int id = t + 256 * q, row = id >> 3, ch = id & 7;
-      *reinterpret_cast<u32x4*>(&As[buf][swz(row, ch)]) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < BCH; ++q) {
-      const int id = t + 256 * q, row = id >> 3, ch = id & 7;
-      *reinterpret_cast<u32x4*>(&Bs[buf][swz(row, ch)]) = rb[q];
+      const void* src = (gk < K && gn < N_valid) ? (const void*)(Bm + (size_t)gn * ldb + gk) : (const void*)g_zero16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + BM * GBK + (q * GNW + w) * 64 * 8), 16, 0, 0);
     }
   };
 
@@ -96,35 +120,47 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
-
-  // rows of this lane's fragments inside the LDS tiles
   int arow[FM], brow[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) arow[i] = wm * WM + i * 32 + ln;
 #pragma unroll
   for (int j = 0; j < FN; ++j) brow[j] = wn * WN + j * 32 + remap_row(ln);
 
-  const int nk = (K + GBK - 1) / GBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GBK);
+  auto compute = [&](int stage) {
+    const uint16_t* As = lds + stage * STAGE;
+    const uint16_t* Bs = As + BM * GBK;
+    u32x4 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = *reinterpret_cast<const u32x4*>(&As[swz(arow[i], h)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = *reinterpret_cast<const u32x4*>(&Bs[swz(brow[j], h)]);
 #pragma unroll
     for (int p = 0; p < GBK / 16; ++p) {
-      u32x4 fa[FM], fb[FN];
+      const int c = p & 1;
+      if (p + 1 < GBK / 16) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&As[cur][swz(arow[i], 2 * p + h)]);
+        for (int i = 0; i < FM; ++i) fa[c ^ 1][i] = *reinterpret_cast<const u32x4*>(&As[swz(arow[i], 2 * (p + 1) + h)]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const u32x4*>(&Bs[cur][swz(brow[j], 2 * p + h)]);
+        for (int j = 0; j < FN; ++j) fb[c ^ 1][j] = *reinterpret_cast<const u32x4*>(&Bs[swz(brow[j], 2 * (p + 1) + h)]);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[c][j], fa[c][i], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    pin_schedule<FM, FN>();
+  };
+
+  const int nk = (K + GBK - 1) / GBK;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this thread's loads of tile kt have landed (nothing later is in flight
+    // yet); the barrier makes every thread's part visible and also guarantees
+    // the other stage is no longer being read before it is refilled
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * GBK);
+    compute(kt & 1);
   }
 
   // ---- epilogue: lane (h, ln) of block (i, j) holds row m0 + wm*WM + 32i + ln,
@@ -142,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     for (int j = 0; j < FN; ++j) {
       const int nb = n0 + wn * WN + 32 * j + 16 * h;
       const floatx16 a = acc[i][j];
-      if (EPI == EPI_ERR) {
+      if (EPI == EPI_ERR && m < M) {   // rows past M were read from a clamped row
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss += a[r] * a[r];
       }
@@ -156,12 +192,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     }
   }
   if (EPI == EPI_ERR) {
-    __shared__ float wsum[4];
+    __syncthreads();                                   // the ring is no longer read
+    float* wsum = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) ss += shfl_xor(ss, x);
     if (l == 0) wsum[w] = ss;
     __syncthreads();
-    if (t == 0) part[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    if (t == 0) {
+      float tot = 0.f;
+      for (int i = 0; i < GNW; ++i) tot += wsum[i];
+      part[blockIdx.x] = tot;
+    }
   }
 }
 
@@ -245,8 +286,12 @@ __global__ __launch_bounds__(256) void error_finalize_kernel(const float* __rest
 }
 
 // ---- launchers -------------------------------------------------------------------
+// error GEMM: 256 x 128 tiles (the 4096 x 2048 residual is exactly 256 tiles);
+// dD GEMM: 256 x 256 tiles.
+constexpr int EBM = 256, EBN = 128, DBM = 256, DBN = 256;
+
 int gemm_error_parts(int M, int N, int bf16) {
-  if (bf16) return ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+  if (bf16) return ((M + EBM - 1) / EBM) * ((N + EBN - 1) / EBN);
   return ((M + 63) / 64) * ((N + 63) / 64);
 }
 
@@ -254,14 +299,16 @@ hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm
                                   int N_valid, int N_store, int K, uint16_t* C, int ldc,
                                   float* part, hipStream_t s) {
   const int G = gemm_error_parts(M, N_store, 1);
-  gemm_bf16_kernel<EPI_ERR><<<G, 256, 0, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr);
+  gemm_bf16_kernel<EBM, EBN, EPI_ERR><<<G, GNT, gemm_lds_bytes<EBM, EBN>(), s>>>(
+      A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
                                int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s) {
-  const int G = gemm_error_parts(M, N, 1);
-  gemm_bf16_kernel<EPI_DD><<<G, 256, 0, s>>>(A, lda, Bm, ldb, M, N, N, K, C, ldc, nullptr, E);
+  const int G = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+  gemm_bf16_kernel<DBM, DBN, EPI_DD><<<G, GNT, gemm_lds_bytes<DBM, DBN>(), s>>>(
+      A, lda, Bm, ldb, M, N, N, K, C, ldc, nullptr, E);
   return hipGetLastError();
 }
 
