@@ -7,31 +7,60 @@
 // rows and writes that partial B x B matrix; the Sinkhorn adjoint kernel adds
 // the chunk partials in chunk order (deterministic, no atomics).
 //
-// bf16 kernel: 4 waves; wave w takes the 32-wide column block t = w % (B/32)
-// of the permuted positions and the 32-row sub-tile w / (B/32). Per sub-tile it
-//   1. forms W_hat[i][k] and Y[i][k] = (G P_b)[i][k] for its 32 positions k
-//      with MFMA (A operand: W or G rows from LDS, row-remapped so that a lane
-//      ends up holding 16 consecutive rows i of one position k; B operand:
-//      P_b fragments prepared in LDS),
-//   2. applies the mask bits, rounds A = W_hat . M and Y . M to bf16,
-//   3. accumulates dP^T[k][j] += sum_i A[i][k] G[i][j] + (Y . M)[i][k] W[i][j]
-//      with MFMA, the rows i in the K slots (the lane's 16 rows are exactly
-//      the K slots it supplies) and G / W columns read from the LDS tiles.
-// Waves sharing t add their accumulators through LDS in a fixed order.
+// bf16 kernel: each wave runs its own pipeline over 32-row tiles of W and G.
+// Tiles move HBM -> LDS with 16-byte direct-to-LDS loads into a private
+// two-stage ring (no register staging, no workgroup barriers in the loop);
+// load instruction (matrix, K step p) of a tile has lane l fetch exactly the
+// 16 bytes that lane l later feeds to the MFMA for that K step, so the LDS
+// reads are linear and conflict-free. Rows are remapped so that MFMA outputs
+// land with 16 consecutive rows per lane. Per tile:
+//   1. W_hat = W P_b and Y = G P_b (MFMA, P_b fragments prepared in LDS),
+//      giving, per lane, one permuted position k and 16 rows i;
+//   2. the tile's mask words (loaded with the tile) turn them into
+//      A = W_hat . M and Y . M, rounded to bf16;
+//   3. G and W are transposed into the same "16 rows per lane" layout by an
+//      MFMA against the identity (exact: bf16 x 1.0 in fp32);
+//   4. dP^T[k][j] += sum_i A[i][k] G[i][j] + (Y . M)[i][k] W[i][j], MFMA with
+//      the rows i in the K slots on both sides.
+// For B = 128 the four waves of a workgroup take the same 32-row tile, share
+// one ring (each wave issues a quarter of the loads, a barrier per tile) and
+// each owns one 32-wide column block of dP (register budget); for B <= 64
+// every wave owns whole tiles and its own ring. Partial sums of waves owning
+// the same columns are added through LDS in a fixed order.
 #include "common.h"
 #include "kernels.h"
 
 namespace lcp {
 
+typedef __attribute__((address_space(3))) void* adj_lds_t;
+__device__ const u32x4 g_adj_zero[1] = {{0u, 0u, 0u, 0u}};
+
 template <int B>
 struct AdjGeom {
-  static constexpr int KS = B / 16;
-  static constexpr int TT = B / 32;
-  static constexpr int RS = 4 / TT;             // 32-row sub-tiles per workgroup tile
-  static constexpr int ROWS = 32 * RS;          // rows per workgroup tile
-  static constexpr int LDT = B + 8;             // padded LDS row (uint16)
+  static constexpr int KS = B / 16;             // K steps over a block
+  static constexpr int TT = B / 32;             // 32-wide column blocks
+  static constexpr int WS = (B == 128) ? 4 : 1; // waves sharing one row tile
+  static constexpr int OWN = TT / WS;           // column blocks (t2) owned per wave
+  static constexpr int TILES = 4 / WS;          // row tiles in flight per workgroup
+  static constexpr int ROWS = 32 * TILES;       // rows per workgroup step
   static constexpr int FRAG = TT * KS * 64;     // u32x4 entries of the P fragments
+  static constexpr int S = 2;                   // ring stages per wave
+  static constexpr int BI = (TT + 1) / 2;       // mask-word load instructions per tile
+  static constexpr int STAGE = 2 * KS * 1024 + BI * 256;   // bytes per stage
+  static constexpr int IPT = 2 * KS + BI;       // load instructions per tile
 };
+
+__device__ __forceinline__ u32x4 identity_slots(int v, int h, int n) {
+  // MFMA B operand of the 32 x 32 identity, K step v: slot e of lane (h, n)
+  // is 1 when column n equals row 16v + 8h + e
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e0 = 16 * v + 8 * h + 2 * q;
+    w[q] = (e0 == n ? 0x3f80u : 0u) | ((e0 + 1 == n ? 0x3f80u : 0u) << 16);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
 
 template <int B>
 __global__ __launch_bounds__(256) void adjoint_bf16_kernel(const uint16_t* __restrict__ G,
@@ -41,21 +70,24 @@ __global__ __launch_bounds__(256) void adjoint_bf16_kernel(const uint16_t* __res
                                                            int cout, int cin, int chunk_rows,
                                                            float* __restrict__ part) {
   using Gm = AdjGeom<B>;
-  constexpr int KS = Gm::KS, TT = Gm::TT, RS = Gm::RS, ROWS = Gm::ROWS, LDT = Gm::LDT;
-  __shared__ __attribute__((aligned(16))) uint16_t fb[Gm::FRAG * 8];
-  // W and G tiles; after the row loop the same space holds the cross-wave sums
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2 * ROWS * LDT];
-  static_assert((RS - 1) * TT * TT * 16 * 64 * 4 <= 2 * ROWS * LDT * 2, "combine buffer");
-  uint16_t* tw = tiles;
-  uint16_t* tg = tiles + ROWS * LDT;
+  constexpr int KS = Gm::KS, TT = Gm::TT, WS = Gm::WS, OWN = Gm::OWN, TILES = Gm::TILES;
+  constexpr int S = Gm::S, STAGE = Gm::STAGE;
+  extern __shared__ __attribute__((aligned(16))) unsigned char adj_lds[];
+  // layout: P fragments | rings (one per row-tile slot, S stages) | cross-wave sums
+  uint16_t* fb = reinterpret_cast<uint16_t*>(adj_lds);
+  unsigned char* rings = adj_lds + Gm::FRAG * 16;
+  float* red = reinterpret_cast<float*>(rings + TILES * S * STAGE);
 
   const int b = blockIdx.x, chunk = blockIdx.y;
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int h = l >> 5, n = l & 31;
-  const int tb = w % TT, rs = w / TT;
+  const int slot = w / WS;          // row tile slot of this wave
+  const int half = w % WS;          // column blocks t2 = half * OWN + o
   const int words = cin >> 5;
+  unsigned char* ring = rings + slot * S * STAGE;
 
-  // P fragments: fb[(t*KS + p)*64 + lane][e] = P_b[16p + 8h + e][32t + n]
+  // P fragments (MFMA B operand, K = source channel j, N = position k):
+  // fb[(t*KS + p)*64 + lane][e] = P_b[16p + 8h + e][32t + n]
   {
     const float* src = P + (size_t)b * B * B;
     for (int e_idx = t; e_idx < B * B; e_idx += 256) {
@@ -64,107 +96,169 @@ __global__ __launch_bounds__(256) void adjoint_bf16_kernel(const uint16_t* __res
       fb[(((tt * KS + p) * 64) + 32 * hh + nn) * 8 + e] = (uint16_t)f2bf(src[e_idx]);
     }
   }
+  __syncthreads();
+  const u32x4* F = reinterpret_cast<const u32x4*>(fb);
 
-  floatx16 acc[TT];
+  floatx16 acc[TT][OWN];
 #pragma unroll
-  for (int q = 0; q < TT; ++q) acc[q] = floatx16{};
+  for (int a = 0; a < TT; ++a)
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) acc[a][o] = floatx16{};
 
   const int r0 = chunk * chunk_rows;
   const int r1 = min(cout, r0 + chunk_rows);
-  const u32x4* F = reinterpret_cast<const u32x4*>(fb);
-  for (int i0 = r0; i0 < r1; i0 += ROWS) {
-    __syncthreads();  // previous tile fully consumed (and fragments written)
-    // cooperative load of ROWS x B of W and G (16-byte chunks)
-    for (int id = t; id < ROWS * (B / 8); id += 256) {
-      const int row = id / (B / 8), ch = id % (B / 8);
-      const int gi = i0 + row;
-      u32x4 vw = {0u, 0u, 0u, 0u}, vg = {0u, 0u, 0u, 0u};
-      if (gi < r1) {
-        const size_t o = (size_t)gi * cin + b * B + ch * 8;
-        vw = *reinterpret_cast<const u32x4*>(W + o);
-        vg = *reinterpret_cast<const u32x4*>(G + o);
-      }
-      *reinterpret_cast<u32x4*>(&tw[row * LDT + ch * 8]) = vw;
-      *reinterpret_cast<u32x4*>(&tg[row * LDT + ch * 8]) = vg;
-    }
-    __syncthreads();
+  const int lrow = remap_row(n);     // tile row whose operands this lane fetches
 
-    // 1. W_hat and Y for positions 32*tb + n, rows 32*rs + 16h + r
-    const int arow = 32 * rs + remap_row(n);
-    floatx16 wh = {}, yy = {};
+  // the load instructions of one tile into stage st (with WS waves sharing a
+  // ring, wave `half` issues every WS-th of them)
+  auto issue = [&](int st, int i0) {
+    unsigned char* sb = ring + st * STAGE;
+    const int i = i0 + lrow;
 #pragma unroll
     for (int p = 0; p < KS; ++p) {
-      const u32x4 fw = *reinterpret_cast<const u32x4*>(&tw[arow * LDT + 16 * p + 8 * h]);
-      const u32x4 fg = *reinterpret_cast<const u32x4*>(&tg[arow * LDT + 16 * p + 8 * h]);
-      const u32x4 fp = F[(tb * KS + p) * 64 + l];
-      wh = mfma32(fw, fp, wh);
-      yy = mfma32(fg, fp, yy);
+      if ((2 * p) % WS != half) continue;
+      const size_t o = (size_t)i * cin + b * B + 16 * p + 8 * h;
+      const void* sw = (i < r1) ? (const void*)(W + o) : (const void*)g_adj_zero;
+      const void* sg = (i < r1) ? (const void*)(G + o) : (const void*)g_adj_zero;
+      __builtin_amdgcn_global_load_lds(sw, (adj_lds_t)(sb + p * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sg, (adj_lds_t)(sb + (KS + p) * 1024), 16, 0, 0);
     }
-    // 2. mask (bit n of word (row, 32*b*B/32 + tb)), round to bf16
-    u32x4 aop[2], yop[2];
+    // mask words: instruction q, lane (h, n) -> word 2q + h of row i0 + n
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float av[8], yv[8];
+    for (int q = 0; q < Gm::BI; ++q) {
+      if (q % WS != half) continue;
+      const int a = (2 * q + h) % TT;
+      const int ib = i0 + n;
+      const void* sbits = (ib < r1) ? (const void*)(bits + (size_t)ib * words + ((b * B) >> 5) + a)
+                                    : (const void*)g_adj_zero;
+      __builtin_amdgcn_global_load_lds(sbits, (adj_lds_t)(sb + 2 * KS * 1024 + q * 256), 4, 0, 0);
+    }
+  };
+
+  const int step = 32 * TILES;
+  const int first = r0 + 32 * slot;
+  const int ntile = (first < r1) ? (r1 - first + step - 1) / step : 0;
+  if (ntile > 0) issue(0, first);
+  for (int it = 0; it < ntile; ++it) {
+    // this wave's loads of tile `it` have landed (nothing later is in flight);
+    // the other stage was consumed in the previous iteration and is refilled.
+    // A shared ring also needs every wave's part and every wave done with the
+    // other stage: one barrier.
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    if (WS > 1) __builtin_amdgcn_s_barrier();
+    if (it + 1 < ntile) issue((it + 1) & 1, first + (it + 1) * step);
+    const unsigned char* sb = ring + (it & 1) * STAGE;
+    const u32x4* LW = reinterpret_cast<const u32x4*>(sb);
+    const u32x4* LG = reinterpret_cast<const u32x4*>(sb + KS * 1024);
+    const uint32_t* LB = reinterpret_cast<const uint32_t*>(sb + 2 * KS * 1024);
+
+    // transposed G and W for the owned column blocks: 16 rows per lane
+    u32x4 gT[OWN][2], wT[OWN][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int gi = i0 + 32 * rs + 16 * h + 8 * u + e;
-        uint32_t keep = 0;
-        if (gi < r1) keep = (bits[(size_t)gi * words + ((b * B) >> 5) + tb] >> n) & 1u;
-        av[e] = keep ? wh[8 * u + e] : 0.f;
-        yv[e] = keep ? yy[8 * u + e] : 0.f;
+    for (int o = 0; o < OWN; ++o) {
+      const int t2 = half * OWN + o;
+      floatx16 tg = {}, tw = {};
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const u32x4 id = identity_slots(v, h, n);
+        tg = mfma32(LG[(2 * t2 + v) * 64 + l], id, tg);
+        tw = mfma32(LW[(2 * t2 + v) * 64 + l], id, tw);
       }
-      aop[u] = u32x4{pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7])};
-      yop[u] = u32x4{pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]), pack2(yv[6], yv[7])};
-    }
-    // 3. dP^T[k][j] += sum_i A[i][k] G[i][j] + Ym[i][k] W[i][j]
-#pragma unroll
-    for (int t2 = 0; t2 < TT; ++t2) {
-      const int col = 32 * t2 + n;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int rb = 32 * rs + 16 * h + 8 * u;
-        uint32_t g4[4], w4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          g4[q] = tg[(rb + 2 * q) * LDT + col] | ((uint32_t)tg[(rb + 2 * q + 1) * LDT + col] << 16);
-          w4[q] = tw[(rb + 2 * q) * LDT + col] | ((uint32_t)tw[(rb + 2 * q + 1) * LDT + col] << 16);
-        }
-        acc[t2] = mfma32(aop[u], u32x4{g4[0], g4[1], g4[2], g4[3]}, acc[t2]);
-        acc[t2] = mfma32(yop[u], u32x4{w4[0], w4[1], w4[2], w4[3]}, acc[t2]);
+        gT[o][u] = u32x4{pack2_exact(tg[8 * u], tg[8 * u + 1]), pack2_exact(tg[8 * u + 2], tg[8 * u + 3]),
+                         pack2_exact(tg[8 * u + 4], tg[8 * u + 5]), pack2_exact(tg[8 * u + 6], tg[8 * u + 7])};
+        wT[o][u] = u32x4{pack2_exact(tw[8 * u], tw[8 * u + 1]), pack2_exact(tw[8 * u + 2], tw[8 * u + 3]),
+                         pack2_exact(tw[8 * u + 4], tw[8 * u + 5]), pack2_exact(tw[8 * u + 6], tw[8 * u + 7])};
       }
     }
-  }
-  __syncthreads();
-
-  // combine the RS waves that share tb (fixed order), then store:
-  // lane (h, n) of block t2 holds dP^T[k = 32tb + 8(r/4) + 4h + r%4][j = 32t2 + n]
-  float* red = reinterpret_cast<float*>(tiles);   // (RS-1) * TT * TT * 16 * 64 floats
-  if (RS > 1 && rs > 0) {
 #pragma unroll
-    for (int t2 = 0; t2 < TT; ++t2)
+    for (int a = 0; a < TT; ++a) {
+      // W_hat and Y for positions 32a + n, rows 16h + r
+      floatx16 wh = {}, yy = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        red[((((rs - 1) * TT + tb) * TT + t2) * 16 + r) * 64 + l] = acc[t2][r];
-  }
-  __syncthreads();
-  if (rs == 0) {
-    for (int s = 1; s < RS; ++s)
-#pragma unroll
-      for (int t2 = 0; t2 < TT; ++t2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t2][r] += red[((((s - 1) * TT + tb) * TT + t2) * 16 + r) * 64 + l];
-    float* dst = part + ((size_t)chunk * (cin / B) + b) * B * B;
-#pragma unroll
-    for (int t2 = 0; t2 < TT; ++t2) {
-      const int j = 32 * t2 + n;
+      for (int p = 0; p < KS; ++p) {
+        const u32x4 fp = F[(a * KS + p) * 64 + l];
+        wh = mfma32(LW[p * 64 + l], fp, wh);
+        yy = mfma32(LG[p * 64 + l], fp, yy);
+      }
+      // mask words of rows 16h + r for column block a (instruction a/2, lane half a%2)
+      const u32x4* mw = reinterpret_cast<const u32x4*>(LB + (a / 2) * 64 + (a % 2) * 32 + 16 * h);
+      uint32_t m16[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int k = 32 * tb + 8 * q + 4 * h;
-        *reinterpret_cast<floatx4*>(dst + j * B + k) =
-            floatx4{acc[t2][4 * q], acc[t2][4 * q + 1], acc[t2][4 * q + 2], acc[t2][4 * q + 3]};
+        const u32x4 v4 = mw[q];
+        m16[4 * q] = v4.x; m16[4 * q + 1] = v4.y; m16[4 * q + 2] = v4.z; m16[4 * q + 3] = v4.w;
+      }
+      u32x4 aop[2], yop[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float av[8], yv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool keep = (m16[8 * u + e] >> n) & 1u;
+          av[e] = keep ? wh[8 * u + e] : 0.f;
+          yv[e] = keep ? yy[8 * u + e] : 0.f;
+        }
+        aop[u] = u32x4{pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7])};
+        yop[u] = u32x4{pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]), pack2(yv[6], yv[7])};
+      }
+#pragma unroll
+      for (int o = 0; o < OWN; ++o)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          acc[a][o] = mfma32(aop[u], gT[o][u], acc[a][o]);
+          acc[a][o] = mfma32(yop[u], wT[o][u], acc[a][o]);
+        }
+    }
+  }
+
+  // lane (h, n) of block (a, o) holds dP^T[k = 32a + 8(r/4) + 4h + r%4][j = 32 t2 + n];
+  // waves owning the same t2 are added into slot 0, one slot per round
+  if (TILES > 1) {
+    for (int s2 = 1; s2 < TILES; ++s2) {
+      __syncthreads();
+      if (slot == s2) {
+#pragma unroll
+        for (int a = 0; a < TT; ++a)
+#pragma unroll
+          for (int o = 0; o < OWN; ++o)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l] = acc[a][o][r];
+      }
+      __syncthreads();
+      if (slot == 0) {
+#pragma unroll
+        for (int a = 0; a < TT; ++a)
+#pragma unroll
+          for (int o = 0; o < OWN; ++o)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][o][r] += red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l];
       }
     }
   }
+  if (slot == 0) {
+    float* dst = part + ((size_t)chunk * (cin / B) + b) * B * B;
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int o = 0; o < OWN; ++o) {
+        const int j = 32 * (half * OWN + o) + n;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = 32 * a + 8 * q + 4 * h;
+          *reinterpret_cast<floatx4*>(dst + j * B + k) =
+              floatx4{acc[a][o][4 * q], acc[a][o][4 * q + 1], acc[a][o][4 * q + 2], acc[a][o][4 * q + 3]};
+        }
+      }
+  }
+}
+
+template <int B>
+constexpr size_t adj_lds_bytes() {
+  using Gm = AdjGeom<B>;
+  return (size_t)Gm::FRAG * 16 + (size_t)Gm::TILES * Gm::S * Gm::STAGE +
+         (Gm::TILES > 1 ? (size_t)Gm::WS * Gm::TT * Gm::OWN * 16 * 64 * 4 : 0);
 }
 
 // fp32 VALU version: one thread per (j, k) group of outputs, rows streamed
@@ -222,9 +316,11 @@ __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restric
   }
 }
 
+static int adjoint_rows_step(int B) { return B == 32 ? AdjGeom<32>::ROWS : B == 64 ? AdjGeom<64>::ROWS : AdjGeom<128>::ROWS; }
+
 int adjoint_chunks(int cout, int nb, int B) {
   int chunks = (1024 + nb - 1) / nb;
-  const int rows_tile = 32 * (4 / (B / 32));
+  const int rows_tile = adjoint_rows_step(B);
   const int max_chunks = (cout + rows_tile - 1) / rows_tile;
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
@@ -232,7 +328,7 @@ int adjoint_chunks(int cout, int nb, int B) {
 }
 
 static int adjoint_chunk_rows(int cout, int chunks, int B) {
-  const int rows_tile = 32 * (4 / (B / 32));
+  const int rows_tile = adjoint_rows_step(B);
   int cr = (cout + chunks - 1) / chunks;
   return (cr + rows_tile - 1) / rows_tile * rows_tile;
 }
@@ -243,9 +339,9 @@ hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const float
   const int cr = adjoint_chunk_rows(cout, chunks, B);
   dim3 grid(cin / B, chunks);
   switch (B) {
-    case 32: adjoint_bf16_kernel<32><<<grid, 256, 0, s>>>(G, W, P, bits, cout, cin, cr, part); break;
-    case 64: adjoint_bf16_kernel<64><<<grid, 256, 0, s>>>(G, W, P, bits, cout, cin, cr, part); break;
-    case 128: adjoint_bf16_kernel<128><<<grid, 256, 0, s>>>(G, W, P, bits, cout, cin, cr, part); break;
+    case 32: adjoint_bf16_kernel<32><<<grid, 256, adj_lds_bytes<32>(), s>>>(G, W, P, bits, cout, cin, cr, part); break;
+    case 64: adjoint_bf16_kernel<64><<<grid, 256, adj_lds_bytes<64>(), s>>>(G, W, P, bits, cout, cin, cr, part); break;
+    case 128: adjoint_bf16_kernel<128><<<grid, 256, adj_lds_bytes<128>(), s>>>(G, W, P, bits, cout, cin, cr, part); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -20,7 +20,19 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (lo in bits 0..15), round-to-nearest-even;
+// one v_cvt_pk_bf16_f32 on gfx950
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+// two floats that are exactly representable in bf16 -> packed pair (upper
+// halves, one v_perm_b32)
+__device__ __forceinline__ uint32_t pack2_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
