@@ -25,8 +25,9 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int pitch_of(int T) { return (T + 63) / 64 * 64; }
 
 struct StepLayout {
-  size_t P, off, bits, D, R, part, E, adj, total;
-  int nb, pitch, nparts, chunks;
+  size_t P, off, bits, D, R, part, E, adj, fragF, fragA, total;
+  int nb, pitch, nparts;
+  AdjSplit sp;
 };
 
 StepLayout step_layout(int cout, int cin, int T, int B, int iters, lcp_dtype dt) {
@@ -34,16 +35,19 @@ StepLayout step_layout(int cout, int cin, int T, int B, int iters, lcp_dtype dt)
   L.nb = cin / B;
   L.pitch = pitch_of(T);
   L.nparts = gemm_error_parts(cout, L.pitch, dt == LCP_BF16);
-  L.chunks = adjoint_chunks(cout, L.nb, B);
+  L.sp = adjoint_split(cout, cin, B);
+  const bool bf = dt == LCP_BF16;
   size_t o = 0;
-  L.P = o;    o += align_up((size_t)L.nb * B * B * 4);
-  L.off = o;  o += align_up((size_t)L.nb * iters * 2 * B * 4);
-  L.bits = o; o += align_up((size_t)cout * (cin / 32) * 4);
-  L.D = o;    o += align_up((size_t)cout * cin * esize(dt));
-  L.R = o;    o += align_up((size_t)cout * L.pitch * esize(dt));
-  L.part = o; o += align_up((size_t)L.nparts * 4);
-  L.E = o;    o += align_up(4);
-  L.adj = o;  o += align_up((size_t)L.chunks * L.nb * B * B * 4);
+  L.P = o;     o += align_up((size_t)L.nb * B * B * 4);
+  L.off = o;   o += align_up((size_t)L.nb * iters * 2 * B * 4);
+  L.bits = o;  o += align_up((size_t)cout * (cin / 32) * 4);
+  L.D = o;     o += align_up((size_t)cout * cin * esize(dt));
+  L.R = o;     o += align_up((size_t)cout * L.pitch * esize(dt));
+  L.part = o;  o += align_up((size_t)L.nparts * 4);
+  L.E = o;     o += align_up(4);
+  L.adj = o;   o += align_up((size_t)L.sp.grid * L.sp.maxseg * B * B * 4);
+  L.fragF = o; o += bf ? align_up((size_t)L.nb * frag_fwd_entries(B) * 16) : 0;
+  L.fragA = o; o += bf ? align_up((size_t)L.nb * frag_adj_entries(B) * 16) : 0;
   L.total = o;
   return L;
 }
@@ -120,7 +124,7 @@ int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B, int it
   if ((long long)iters * B > kMaxIterB) return LCP_E_UNSUPPORTED;
   if (!fits_i32(nb, (long long)B * B) || !aligned16(logits) || !aligned16(dP) || !aligned16(dlogits))
     return LCP_E_INVAL;
-  LCP_RUN(launch_sinkhorn_bwd(logits, dP, 1, 0, nullptr, dlogits, nb, B, iters, tau, S(stream)));
+  LCP_RUN(launch_sinkhorn_bwd(logits, dP, nullptr, nullptr, dlogits, nb, B, iters, tau, S(stream)));
   return LCP_OK;
 }
 
@@ -161,8 +165,8 @@ int lcp_permute(const void* A, lcp_dtype adt, int rows, int cin, const float* co
   if (mode == PERM_IMPORTANCE && odt != LCP_F32) return LCP_E_UNSUPPORTED;
   if (adt == LCP_F32 && odt != LCP_F32) return LCP_E_UNSUPPORTED;
   if (adt == LCP_BF16) {
-    LCP_RUN(launch_permute_bf16((const uint16_t*)A, rows, cin, colscale, P, B, transposeP ? 1 : 0, mode, out,
-                                odt == LCP_F32, nullptr, 0, 4, S(stream)));
+    LCP_RUN(launch_permute_bf16((const uint16_t*)A, rows, cin, colscale, P, B, transposeP ? 1 : 0, nullptr,
+                                mode, out, odt == LCP_F32, nullptr, 0, 4, S(stream)));
   } else {
     LCP_RUN(launch_permute_f32((const float*)A, rows, cin, colscale, P, B, transposeP ? 1 : 0, mode,
                                (float*)out, nullptr, 0, 4, S(stream)));
@@ -251,13 +255,20 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
   const Timer tmr{tm, s};
   const bool bf = L->dtype == LCP_BF16;
 
+  u32x4* fragF = (u32x4*)(base + Ly.fragF);
+  u32x4* fragA = (u32x4*)(base + Ly.fragA);
   tmr.start(0);
   LCP_RUN(launch_sinkhorn_fwd(logits, P, off, Ly.nb, L->B, c->iters, c->tau, s));
   tmr.stop(0);
+  if (bf) {
+    tmr.start(4);
+    LCP_RUN(launch_frag(P, L->norms, Ly.nb, L->B, fragF, fragA, s));
+    tmr.stop(4);
+  }
   tmr.start(1);
   if (bf)
-    LCP_RUN(launch_permute_bf16((const uint16_t*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, PERM_FWD, D, 0,
-                                bits, c->N, c->M, s));
+    LCP_RUN(launch_permute_bf16((const uint16_t*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, fragF, PERM_FWD,
+                                D, 0, bits, c->N, c->M, s));
   else
     LCP_RUN(launch_permute_f32((const float*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, PERM_FWD, (float*)D,
                                bits, c->N, c->M, s));
@@ -310,17 +321,17 @@ int lcp_step_bwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
     LCP_RUN(launch_gemm_dd_f32((const float*)R, Ly.pitch, (const float*)L->X, L->cin, L->cout, L->cin, L->T, Ews,
                                (float*)Gd, L->cin, s));
   tmr.stop(0);
+  const u32x4* fragA = (const u32x4*)(base + Ly.fragA);
   tmr.start(1);
   if (bf)
-    LCP_RUN(launch_adjoint_bf16((const uint16_t*)Gd, (const uint16_t*)L->W, P, bits, L->cout, L->cin, L->B,
-                                Ly.chunks, adj, s));
+    LCP_RUN(launch_adjoint_bf16((const uint16_t*)Gd, (const uint16_t*)L->W, fragA, P, bits, L->cout, L->cin,
+                                L->B, Ly.sp, adj, s));
   else
-    LCP_RUN(launch_adjoint_f32((const float*)Gd, (const float*)L->W, P, bits, L->cout, L->cin, L->B, Ly.chunks,
+    LCP_RUN(launch_adjoint_f32((const float*)Gd, (const float*)L->W, P, bits, L->cout, L->cin, L->B, Ly.sp,
                                adj, s));
   tmr.stop(1);
   tmr.start(2);
-  LCP_RUN(launch_sinkhorn_bwd(logits, adj, Ly.chunks, (size_t)Ly.nb * L->B * L->B, off, dlogits, Ly.nb, L->B,
-                              c->iters, c->tau, s));
+  LCP_RUN(launch_sinkhorn_bwd(logits, adj, &Ly.sp, off, dlogits, Ly.nb, L->B, c->iters, c->tau, s));
   tmr.stop(2);
   return LCP_OK;
 }

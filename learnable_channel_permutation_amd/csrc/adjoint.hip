@@ -62,300 +62,325 @@ __device__ __forceinline__ u32x4 identity_slots(int v, int h, int n) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// Persistent grid: workgroup g takes the contiguous range [g*tpw, (g+1)*tpw)
+// of the block-major sequence of 32-row tiles (tpb tiles per block), which
+// spans at most `maxseg` blocks; it writes one partial B x B matrix per block
+// segment to part[(g * maxseg + k) * B * B] (k = block - first block of g).
 template <int B>
-__global__ __launch_bounds__(256) void adjoint_bf16_kernel(const uint16_t* __restrict__ G,
-                                                           const uint16_t* __restrict__ W,
-                                                           const float* __restrict__ P,
-                                                           const uint32_t* __restrict__ bits,
-                                                           int cout, int cin, int chunk_rows,
-                                                           float* __restrict__ part) {
+__global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
+    const uint16_t* __restrict__ G, const uint16_t* __restrict__ W, const u32x4* __restrict__ gfrag,
+    const float* __restrict__ P, const uint32_t* __restrict__ bits, int cout, int cin, int tpw,
+    int maxseg, float* __restrict__ part) {
   using Gm = AdjGeom<B>;
   constexpr int KS = Gm::KS, TT = Gm::TT, WS = Gm::WS, OWN = Gm::OWN, TILES = Gm::TILES;
   constexpr int S = Gm::S, STAGE = Gm::STAGE;
   extern __shared__ __attribute__((aligned(16))) unsigned char adj_lds[];
-  // layout: P fragments | rings (one per row-tile slot, S stages) | cross-wave sums
+  // layout: P fragments | rings (one per row-tile slot, S stages); after the
+  // tile loop of a segment the rings hold the cross-wave sums
   uint16_t* fb = reinterpret_cast<uint16_t*>(adj_lds);
   unsigned char* rings = adj_lds + Gm::FRAG * 16;
-  float* red = reinterpret_cast<float*>(rings + TILES * S * STAGE);
+  float* red = reinterpret_cast<float*>(rings);
 
-  const int b = blockIdx.x, chunk = blockIdx.y;
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int h = l >> 5, n = l & 31;
   const int slot = w / WS;          // row tile slot of this wave
   const int half = w % WS;          // column blocks t2 = half * OWN + o
   const int words = cin >> 5;
   unsigned char* ring = rings + slot * S * STAGE;
-
-  // P fragments (MFMA B operand, K = source channel j, N = position k):
-  // fb[(t*KS + p)*64 + lane][e] = P_b[16p + 8h + e][32t + n]
-  {
-    const float* src = P + (size_t)b * B * B;
-    for (int e_idx = t; e_idx < B * B; e_idx += 256) {
-      const int j = e_idx / B, k = e_idx % B;
-      const int tt = k >> 5, nn = k & 31, p = j >> 4, hh = (j >> 3) & 1, e = j & 7;
-      fb[(((tt * KS + p) * 64) + 32 * hh + nn) * 8 + e] = (uint16_t)f2bf(src[e_idx]);
-    }
-  }
-  __syncthreads();
   const u32x4* F = reinterpret_cast<const u32x4*>(fb);
+  const int lrow = remap_row(n);    // tile row whose operands this lane fetches
 
-  floatx16 acc[TT][OWN];
-#pragma unroll
-  for (int a = 0; a < TT; ++a)
-#pragma unroll
-    for (int o = 0; o < OWN; ++o) acc[a][o] = floatx16{};
+  const int tpb = (cout + 31) / 32;
+  const int total = (cin / B) * tpb;
+  const int t_begin = blockIdx.x * tpw;
+  const int t_end = min(total, t_begin + tpw);
+  const int first_b = t_begin / tpb;
 
-  const int r0 = chunk * chunk_rows;
-  const int r1 = min(cout, r0 + chunk_rows);
-  const int lrow = remap_row(n);     // tile row whose operands this lane fetches
-
-  // the load instructions of one tile into stage st (with WS waves sharing a
-  // ring, wave `half` issues every WS-th of them)
-  auto issue = [&](int st, int i0) {
-    unsigned char* sb = ring + st * STAGE;
-    const int i = i0 + lrow;
-#pragma unroll
-    for (int p = 0; p < KS; ++p) {
-      if ((2 * p) % WS != half) continue;
-      const size_t o = (size_t)i * cin + b * B + 16 * p + 8 * h;
-      const void* sw = (i < r1) ? (const void*)(W + o) : (const void*)g_adj_zero;
-      const void* sg = (i < r1) ? (const void*)(G + o) : (const void*)g_adj_zero;
-      __builtin_amdgcn_global_load_lds(sw, (adj_lds_t)(sb + p * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(sg, (adj_lds_t)(sb + (KS + p) * 1024), 16, 0, 0);
-    }
-    // mask words: instruction q, lane (h, n) -> word 2q + h of row i0 + n
-#pragma unroll
-    for (int q = 0; q < Gm::BI; ++q) {
-      if (q % WS != half) continue;
-      const int a = (2 * q + h) % TT;
-      const int ib = i0 + n;
-      const void* sbits = (ib < r1) ? (const void*)(bits + (size_t)ib * words + ((b * B) >> 5) + a)
-                                    : (const void*)g_adj_zero;
-      __builtin_amdgcn_global_load_lds(sbits, (adj_lds_t)(sb + 2 * KS * 1024 + q * 256), 4, 0, 0);
-    }
-  };
-
-  const int step = 32 * TILES;
-  const int first = r0 + 32 * slot;
-  const int ntile = (first < r1) ? (r1 - first + step - 1) / step : 0;
-  if (ntile > 0) issue(0, first);
-  for (int it = 0; it < ntile; ++it) {
-    // this wave's loads of tile `it` have landed (nothing later is in flight);
-    // the other stage was consumed in the previous iteration and is refilled.
-    // A shared ring also needs every wave's part and every wave done with the
-    // other stage: one barrier.
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    if (WS > 1) __builtin_amdgcn_s_barrier();
-    if (it + 1 < ntile) issue((it + 1) & 1, first + (it + 1) * step);
-    const unsigned char* sb = ring + (it & 1) * STAGE;
-    const u32x4* LW = reinterpret_cast<const u32x4*>(sb);
-    const u32x4* LG = reinterpret_cast<const u32x4*>(sb + KS * 1024);
-    const uint32_t* LB = reinterpret_cast<const uint32_t*>(sb + 2 * KS * 1024);
-
-    // transposed G and W for the owned column blocks: 16 rows per lane
-    u32x4 gT[OWN][2], wT[OWN][2];
-#pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-      const int t2 = half * OWN + o;
-      floatx16 tg = {}, tw = {};
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const u32x4 id = identity_slots(v, h, n);
-        tg = mfma32(LG[(2 * t2 + v) * 64 + l], id, tg);
-        tw = mfma32(LW[(2 * t2 + v) * 64 + l], id, tw);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        gT[o][u] = u32x4{pack2_exact(tg[8 * u], tg[8 * u + 1]), pack2_exact(tg[8 * u + 2], tg[8 * u + 3]),
-                         pack2_exact(tg[8 * u + 4], tg[8 * u + 5]), pack2_exact(tg[8 * u + 6], tg[8 * u + 7])};
-        wT[o][u] = u32x4{pack2_exact(tw[8 * u], tw[8 * u + 1]), pack2_exact(tw[8 * u + 2], tw[8 * u + 3]),
-                         pack2_exact(tw[8 * u + 4], tw[8 * u + 5]), pack2_exact(tw[8 * u + 6], tw[8 * u + 7])};
+  for (int seg = t_begin; seg < t_end;) {
+    const int b = seg / tpb;
+    const int seg_end = min(t_end, (b + 1) * tpb);
+    __syncthreads();                       // fragments and sums of the previous block consumed
+    // P fragments (MFMA B operand, K = source channel j, N = position k):
+    // F[(t*KS + p)*64 + lane][e] = P_b[16p + 8h + e][32t + n]
+    if (gfrag != nullptr) {
+      const u32x4* src = gfrag + (size_t)b * Gm::FRAG;
+      u32x4* dst = reinterpret_cast<u32x4*>(fb);
+      for (int e = t; e < Gm::FRAG; e += 256) dst[e] = src[e];
+    } else {
+      const float* src = P + (size_t)b * B * B;
+      for (int e_idx = t; e_idx < B * B; e_idx += 256) {
+        const int j = e_idx / B, k = e_idx % B;
+        const int tt = k >> 5, nn = k & 31, p = j >> 4, hh = (j >> 3) & 1, e = j & 7;
+        fb[(((tt * KS + p) * 64) + 32 * hh + nn) * 8 + e] = (uint16_t)f2bf(src[e_idx]);
       }
     }
-#pragma unroll
-    for (int a = 0; a < TT; ++a) {
-      // W_hat and Y for positions 32a + n, rows 16h + r
-      floatx16 wh = {}, yy = {};
-#pragma unroll
-      for (int p = 0; p < KS; ++p) {
-        const u32x4 fp = F[(a * KS + p) * 64 + l];
-        wh = mfma32(LW[p * 64 + l], fp, wh);
-        yy = mfma32(LG[p * 64 + l], fp, yy);
-      }
-      // mask words of rows 16h + r for column block a (instruction a/2, lane half a%2)
-      const u32x4* mw = reinterpret_cast<const u32x4*>(LB + (a / 2) * 64 + (a % 2) * 32 + 16 * h);
-      uint32_t m16[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 v4 = mw[q];
-        m16[4 * q] = v4.x; m16[4 * q + 1] = v4.y; m16[4 * q + 2] = v4.z; m16[4 * q + 3] = v4.w;
-      }
-      u32x4 aop[2], yop[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float av[8], yv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool keep = (m16[8 * u + e] >> n) & 1u;
-          av[e] = keep ? wh[8 * u + e] : 0.f;
-          yv[e] = keep ? yy[8 * u + e] : 0.f;
-        }
-        aop[u] = u32x4{pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7])};
-        yop[u] = u32x4{pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]), pack2(yv[6], yv[7])};
-      }
-#pragma unroll
-      for (int o = 0; o < OWN; ++o)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          acc[a][o] = mfma32(aop[u], gT[o][u], acc[a][o]);
-          acc[a][o] = mfma32(yop[u], wT[o][u], acc[a][o]);
-        }
-    }
-  }
+    __syncthreads();
 
-  // lane (h, n) of block (a, o) holds dP^T[k = 32a + 8(r/4) + 4h + r%4][j = 32 t2 + n];
-  // waves owning the same t2 are added into slot 0, one slot per round
-  if (TILES > 1) {
-    for (int s2 = 1; s2 < TILES; ++s2) {
-      __syncthreads();
-      if (slot == s2) {
-#pragma unroll
-        for (int a = 0; a < TT; ++a)
-#pragma unroll
-          for (int o = 0; o < OWN; ++o)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l] = acc[a][o][r];
-      }
-      __syncthreads();
-      if (slot == 0) {
-#pragma unroll
-        for (int a = 0; a < TT; ++a)
-#pragma unroll
-          for (int o = 0; o < OWN; ++o)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][o][r] += red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l];
-      }
-    }
-  }
-  if (slot == 0) {
-    float* dst = part + ((size_t)chunk * (cin / B) + b) * B * B;
+    floatx16 acc[TT][OWN];
 #pragma unroll
     for (int a = 0; a < TT; ++a)
 #pragma unroll
-      for (int o = 0; o < OWN; ++o) {
-        const int j = 32 * (half * OWN + o) + n;
+      for (int o = 0; o < OWN; ++o) acc[a][o] = floatx16{};
+
+    // the load instructions of one tile into stage st (with WS waves sharing a
+    // ring, wave `half` issues every WS-th of them)
+    auto issue = [&](int st, int tile) {
+      unsigned char* sb = ring + st * STAGE;
+      const int i0 = (tile - b * tpb) * 32;
+      const int i = i0 + lrow;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int k = 32 * a + 8 * q + 4 * h;
-          *reinterpret_cast<floatx4*>(dst + j * B + k) =
-              floatx4{acc[a][o][4 * q], acc[a][o][4 * q + 1], acc[a][o][4 * q + 2], acc[a][o][4 * q + 3]};
+      for (int p = 0; p < KS; ++p) {
+        if ((2 * p) % WS != half) continue;
+        const size_t o = (size_t)i * cin + b * B + 16 * p + 8 * h;
+        const void* sw = (i < cout) ? (const void*)(W + o) : (const void*)g_adj_zero;
+        const void* sg = (i < cout) ? (const void*)(G + o) : (const void*)g_adj_zero;
+        __builtin_amdgcn_global_load_lds(sw, (adj_lds_t)(sb + p * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(sg, (adj_lds_t)(sb + (KS + p) * 1024), 16, 0, 0);
+      }
+      // mask words: instruction q, lane (h, n) -> word 2q + h of row i0 + n
+#pragma unroll
+      for (int q = 0; q < Gm::BI; ++q) {
+        if (q % WS != half) continue;
+        const int a = (2 * q + h) % TT;
+        const int ib = i0 + n;
+        const void* sbits = (ib < cout) ? (const void*)(bits + (size_t)ib * words + ((b * B) >> 5) + a)
+                                        : (const void*)g_adj_zero;
+        __builtin_amdgcn_global_load_lds(sbits, (adj_lds_t)(sb + 2 * KS * 1024 + q * 256), 4, 0, 0);
+      }
+    };
+
+    const int first = seg + slot;
+    const int ntile = (first < seg_end) ? (seg_end - first + TILES - 1) / TILES : 0;
+    if (ntile > 0) issue(0, first);
+    for (int it = 0; it < ntile; ++it) {
+      // this wave's loads of tile `it` have landed (nothing later is in flight);
+      // the other stage was consumed in the previous iteration and is refilled.
+      // A shared ring also needs every wave's part and every wave done with the
+      // other stage: one barrier.
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+      if (WS > 1) __builtin_amdgcn_s_barrier();
+      if (it + 1 < ntile) issue((it + 1) & 1, first + (it + 1) * TILES);
+      const unsigned char* sb = ring + (it & 1) * STAGE;
+      const u32x4* LW = reinterpret_cast<const u32x4*>(sb);
+      const u32x4* LG = reinterpret_cast<const u32x4*>(sb + KS * 1024);
+      const uint32_t* LB = reinterpret_cast<const uint32_t*>(sb + 2 * KS * 1024);
+
+      // transposed G and W for the owned column blocks: 16 rows per lane
+      u32x4 gT[OWN][2], wT[OWN][2];
+#pragma unroll
+      for (int o = 0; o < OWN; ++o) {
+        const int t2 = half * OWN + o;
+        floatx16 tg = {}, tw = {};
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const u32x4 id = identity_slots(v, h, n);
+          tg = mfma32(LG[(2 * t2 + v) * 64 + l], id, tg);
+          tw = mfma32(LW[(2 * t2 + v) * 64 + l], id, tw);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          gT[o][u] = u32x4{pack2_exact(tg[8 * u], tg[8 * u + 1]), pack2_exact(tg[8 * u + 2], tg[8 * u + 3]),
+                           pack2_exact(tg[8 * u + 4], tg[8 * u + 5]), pack2_exact(tg[8 * u + 6], tg[8 * u + 7])};
+          wT[o][u] = u32x4{pack2_exact(tw[8 * u], tw[8 * u + 1]), pack2_exact(tw[8 * u + 2], tw[8 * u + 3]),
+                           pack2_exact(tw[8 * u + 4], tw[8 * u + 5]), pack2_exact(tw[8 * u + 6], tw[8 * u + 7])};
         }
       }
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        // W_hat and Y for positions 32a + n, rows 16h + r
+        floatx16 wh = {}, yy = {};
+#pragma unroll
+        for (int p = 0; p < KS; ++p) {
+          const u32x4 fp = F[(a * KS + p) * 64 + l];
+          wh = mfma32(LW[p * 64 + l], fp, wh);
+          yy = mfma32(LG[p * 64 + l], fp, yy);
+        }
+        // mask words of rows 16h + r for column block a (instruction a/2, lane half a%2)
+        const u32x4* mw = reinterpret_cast<const u32x4*>(LB + (a / 2) * 64 + (a % 2) * 32 + 16 * h);
+        uint32_t m16[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v4 = mw[q];
+          m16[4 * q] = v4.x; m16[4 * q + 1] = v4.y; m16[4 * q + 2] = v4.z; m16[4 * q + 3] = v4.w;
+        }
+        u32x4 aop[2], yop[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float av[8], yv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool keep = (m16[8 * u + e] >> n) & 1u;
+            av[e] = keep ? wh[8 * u + e] : 0.f;
+            yv[e] = keep ? yy[8 * u + e] : 0.f;
+          }
+          aop[u] = u32x4{pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7])};
+          yop[u] = u32x4{pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]), pack2(yv[6], yv[7])};
+        }
+#pragma unroll
+        for (int o = 0; o < OWN; ++o)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            acc[a][o] = mfma32(aop[u], gT[o][u], acc[a][o]);
+            acc[a][o] = mfma32(yop[u], wT[o][u], acc[a][o]);
+          }
+      }
+    }
+
+    // lane (h, n) of block (a, o) holds dP^T[k = 32a + 8(r/4) + 4h + r%4][j = 32 t2 + n];
+    // waves owning the same t2 are added into slot 0, one slot per round
+    if (TILES > 1) {
+      for (int s2 = 1; s2 < TILES; ++s2) {
+        __syncthreads();
+        if (slot == s2) {
+#pragma unroll
+          for (int a = 0; a < TT; ++a)
+#pragma unroll
+            for (int o = 0; o < OWN; ++o)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l] = acc[a][o][r];
+        }
+        __syncthreads();
+        if (slot == 0) {
+#pragma unroll
+          for (int a = 0; a < TT; ++a)
+#pragma unroll
+            for (int o = 0; o < OWN; ++o)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[a][o][r] += red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l];
+        }
+      }
+    }
+    if (slot == 0) {
+      float* dst = part + ((size_t)blockIdx.x * maxseg + (b - first_b)) * B * B;
+#pragma unroll
+      for (int a = 0; a < TT; ++a)
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+          const int j = 32 * (half * OWN + o) + n;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int k = 32 * a + 8 * q + 4 * h;
+            *reinterpret_cast<floatx4*>(dst + j * B + k) =
+                floatx4{acc[a][o][4 * q], acc[a][o][4 * q + 1], acc[a][o][4 * q + 2], acc[a][o][4 * q + 3]};
+          }
+        }
+    }
+    seg = seg_end;
   }
 }
 
 template <int B>
 constexpr size_t adj_lds_bytes() {
   using Gm = AdjGeom<B>;
-  return (size_t)Gm::FRAG * 16 + (size_t)Gm::TILES * Gm::S * Gm::STAGE +
-         (Gm::TILES > 1 ? (size_t)Gm::WS * Gm::TT * Gm::OWN * 16 * 64 * 4 : 0);
+  const size_t ring = (size_t)Gm::TILES * Gm::S * Gm::STAGE;
+  const size_t red = Gm::TILES > 1 ? (size_t)Gm::WS * Gm::TT * Gm::OWN * 16 * 64 * 4 : 0;
+  return (size_t)Gm::FRAG * 16 + (ring > red ? ring : red);
 }
 
-// fp32 VALU version: one thread per (j, k) group of outputs, rows streamed
-// through LDS one at a time.
+// fp32 VALU version: one thread per group of (j, k) outputs, rows streamed
+// through LDS one at a time; same persistent tile ranges and (workgroup,
+// segment) partial layout as the bf16 kernel.
 template <int B>
 __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restrict__ G,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ P,
                                                           const uint32_t* __restrict__ bits,
-                                                          int cout, int cin, int chunk_rows,
+                                                          int cout, int cin, int tpw, int maxseg,
                                                           float* __restrict__ part) {
   constexpr int PER = (B * B + 255) / 256;
   __shared__ float pb[B][B + 1];
   __shared__ float wr[B], gr[B], am[B], ym[B];
-  const int b = blockIdx.x, chunk = blockIdx.y, t = threadIdx.x;
-  const float* src = P + (size_t)b * B * B;
-  for (int e = t; e < B * B; e += 256) pb[e / B][e % B] = src[e];
-  float acc[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) acc[q] = 0.f;
-  const int r0 = chunk * chunk_rows, r1 = min(cout, r0 + chunk_rows);
+  const int t = threadIdx.x;
   const int words = cin >> 5;
-  for (int i = r0; i < r1; ++i) {
+  const int tpb = (cout + 31) / 32;
+  const int total = (cin / B) * tpb;
+  const int t_begin = blockIdx.x * tpw;
+  const int t_end = min(total, t_begin + tpw);
+  const int first_b = t_begin / tpb;
+  for (int seg = t_begin; seg < t_end;) {
+    const int b = seg / tpb;
+    const int seg_end = min(t_end, (b + 1) * tpb);
     __syncthreads();
-    if (t < B) {
-      wr[t] = W[(size_t)i * cin + b * B + t];
-      gr[t] = G[(size_t)i * cin + b * B + t];
-    }
-    __syncthreads();
-    if (t < B) {
-      float s1 = 0.f, s2 = 0.f;
-      for (int j = 0; j < B; ++j) {
-        s1 = fmaf(wr[j], pb[j][t], s1);
-        s2 = fmaf(gr[j], pb[j][t], s2);
+    const float* src = P + (size_t)b * B * B;
+    for (int e = t; e < B * B; e += 256) pb[e / B][e % B] = src[e];
+    float acc[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) acc[q] = 0.f;
+    const int r0 = (seg - b * tpb) * 32;
+    const int r1 = min(cout, (seg_end - b * tpb) * 32);
+    for (int i = r0; i < r1; ++i) {
+      __syncthreads();
+      if (t < B) {
+        wr[t] = W[(size_t)i * cin + b * B + t];
+        gr[t] = G[(size_t)i * cin + b * B + t];
       }
-      const uint32_t keep = (bits[(size_t)i * words + ((b * B + t) >> 5)] >> (t & 31)) & 1u;
-      am[t] = keep ? s1 : 0.f;
-      ym[t] = keep ? s2 : 0.f;
+      __syncthreads();
+      if (t < B) {
+        float s1 = 0.f, s2 = 0.f;
+        for (int j = 0; j < B; ++j) {
+          s1 = fmaf(wr[j], pb[j][t], s1);
+          s2 = fmaf(gr[j], pb[j][t], s2);
+        }
+        const uint32_t keep = (bits[(size_t)i * words + ((b * B + t) >> 5)] >> (t & 31)) & 1u;
+        am[t] = keep ? s1 : 0.f;
+        ym[t] = keep ? s2 : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int e = t + 256 * q;
+        if (e < B * B) {
+          const int j = e / B, k = e % B;
+          acc[q] = fmaf(gr[j], am[k], fmaf(wr[j], ym[k], acc[q]));
+        }
+      }
     }
-    __syncthreads();
+    float* dst = part + ((size_t)blockIdx.x * maxseg + (b - first_b)) * B * B;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int e = t + 256 * q;
-      if (e < B * B) {
-        const int j = e / B, k = e % B;
-        acc[q] = fmaf(gr[j], am[k], fmaf(wr[j], ym[k], acc[q]));
-      }
+      if (e < B * B) dst[e] = acc[q];
     }
-  }
-  float* dst = part + ((size_t)chunk * (cin / B) + b) * B * B;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int e = t + 256 * q;
-    if (e < B * B) dst[e] = acc[q];
+    seg = seg_end;
   }
 }
 
-static int adjoint_rows_step(int B) { return B == 32 ? AdjGeom<32>::ROWS : B == 64 ? AdjGeom<64>::ROWS : AdjGeom<128>::ROWS; }
-
-int adjoint_chunks(int cout, int nb, int B) {
-  int chunks = (1024 + nb - 1) / nb;
-  const int rows_tile = adjoint_rows_step(B);
-  const int max_chunks = (cout + rows_tile - 1) / rows_tile;
-  if (chunks > max_chunks) chunks = max_chunks;
-  if (chunks < 1) chunks = 1;
-  return chunks;
+// Fixed grids (two resident workgroups per CU on 256 CUs for B <= 64, one
+// for B = 128), independent of the device, so the work split and every result
+// are the same everywhere.
+AdjSplit adjoint_split(int cout, int cin, int B) {
+  AdjSplit sp{};
+  const int tpb = (cout + 31) / 32;
+  const int total = (cin / B) * tpb;
+  int grid = (B == 128) ? 256 : 512;
+  sp.tpw = (total + grid - 1) / grid;
+  sp.grid = (total + sp.tpw - 1) / sp.tpw;
+  sp.maxseg = (sp.tpw + tpb - 1) / tpb + 1;
+  sp.tpb = tpb;
+  return sp;
 }
 
-static int adjoint_chunk_rows(int cout, int chunks, int B) {
-  const int rows_tile = adjoint_rows_step(B);
-  int cr = (cout + chunks - 1) / chunks;
-  return (cr + rows_tile - 1) / rows_tile * rows_tile;
-}
-
-hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const float* P,
-                               const uint32_t* bits, int cout, int cin, int B, int chunks,
+hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const u32x4* gfrag, const float* P,
+                               const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
                                float* part, hipStream_t s) {
-  const int cr = adjoint_chunk_rows(cout, chunks, B);
-  dim3 grid(cin / B, chunks);
   switch (B) {
-    case 32: adjoint_bf16_kernel<32><<<grid, 256, adj_lds_bytes<32>(), s>>>(G, W, P, bits, cout, cin, cr, part); break;
-    case 64: adjoint_bf16_kernel<64><<<grid, 256, adj_lds_bytes<64>(), s>>>(G, W, P, bits, cout, cin, cr, part); break;
-    case 128: adjoint_bf16_kernel<128><<<grid, 256, adj_lds_bytes<128>(), s>>>(G, W, P, bits, cout, cin, cr, part); break;
+    case 32: adjoint_bf16_kernel<32><<<sp.grid, 256, adj_lds_bytes<32>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
+    case 64: adjoint_bf16_kernel<64><<<sp.grid, 256, adj_lds_bytes<64>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
+    case 128: adjoint_bf16_kernel<128><<<sp.grid, 256, adj_lds_bytes<128>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// fp32 kernel: one workgroup per (block, 32-row tile range of one segment),
+// written in the same (workgroup, segment) partial layout as the bf16 kernel.
 hipError_t launch_adjoint_f32(const float* G, const float* W, const float* P,
-                              const uint32_t* bits, int cout, int cin, int B, int chunks,
+                              const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
                               float* part, hipStream_t s) {
-  const int cr = adjoint_chunk_rows(cout, chunks, B);
-  dim3 grid(cin / B, chunks);
   switch (B) {
-    case 32: adjoint_f32_kernel<32><<<grid, 256, 0, s>>>(G, W, P, bits, cout, cin, cr, part); break;
-    case 64: adjoint_f32_kernel<64><<<grid, 256, 0, s>>>(G, W, P, bits, cout, cin, cr, part); break;
-    case 128: adjoint_f32_kernel<128><<<grid, 256, 0, s>>>(G, W, P, bits, cout, cin, cr, part); break;
+    case 32: adjoint_f32_kernel<32><<<sp.grid, 256, 0, s>>>(G, W, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
+    case 64: adjoint_f32_kernel<64><<<sp.grid, 256, 0, s>>>(G, W, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
+    case 128: adjoint_f32_kernel<128><<<sp.grid, 256, 0, s>>>(G, W, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -64,23 +64,29 @@ __device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x
 // ---- N:M keep decision ------------------------------------------------------
 // Position k of a group is kept iff
 //   #{j: v_j > v_k} + #{j < k: v_j == v_k} < N
-// (ties to the lower position). NaN is read as -inf; IEEE compares treat
-// -0 == +0. Returns an M-bit mask, bit k = kept.
-__device__ __forceinline__ float nan_to_ninf(float v) { return (v != v) ? -__builtin_inff() : v; }
+// (ties to the lower position). NaN is read as -inf (IEEE max returns the
+// non-NaN operand); IEEE compares treat -0 == +0. With NaN gone, for j < k
+// the pair contributes [v_j >= v_k] to k's rank and the complement
+// [v_k > v_j] to j's, so each pair is compared once. Returns an M-bit mask,
+// bit k = kept.
+__device__ __forceinline__ float nan_to_ninf(float v) { return __builtin_fmaxf(v, -__builtin_inff()); }
 
 template <int M>
 __device__ __forceinline__ uint32_t nm_keep(const float* v, int N) {
+  int rank[M];
+#pragma unroll
+  for (int k = 0; k < M; ++k) rank[k] = 0;
+#pragma unroll
+  for (int k = 1; k < M; ++k)
+#pragma unroll
+    for (int j = 0; j < k; ++j) {
+      const int c = v[j] >= v[k];
+      rank[k] += c;
+      rank[j] += 1 - c;
+    }
   uint32_t bits = 0;
 #pragma unroll
-  for (int k = 0; k < M; ++k) {
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-      if (j == k) continue;
-      rank += (v[j] > v[k]) || (j < k && v[j] == v[k]);
-    }
-    bits |= (uint32_t)(rank < N) << k;
-  }
+  for (int k = 0; k < M; ++k) bits |= (uint32_t)(rank[k] < N) << k;
   return bits;
 }
 

@@ -7,12 +7,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace lcp {
+
+// Work split of the block adjoint (see below).
+struct AdjSplit {
+  int grid, tpw, tpb, maxseg;
+};
 
 // Sinkhorn (sinkhorn.hip)
 hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb, int B,
                                int iters, float tau, hipStream_t s);
-hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, int parts, size_t part_stride,
+// dP is either dense [nb][B][B] (seg == nullptr) or the block adjoint's
+// (workgroup, segment) partials described by seg, summed in workgroup order.
+hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, const AdjSplit* seg,
                                const float* off, float* dlogits, int nb, int B, int iters,
                                float tau, hipStream_t s);
 
@@ -31,9 +40,17 @@ enum PermMode {
   PERM_IMPORTANCE = 1,  // out = (|A| colscale) P_B, fp32, float32-accurate
   PERM_FWD = 2          // D = W - ((W P_B) . M) P_B^T and mask bits from (|W| n) P_B
 };
+// gfrag (nullable, forward mode only): precomputed fragments from launch_frag.
 hipError_t launch_permute_bf16(const uint16_t* A, int rows, int cin, const float* colscale,
-                               const float* P, int B, int transposeP, int mode, void* out,
-                               int out_f32, uint32_t* bits, int N, int M, hipStream_t s);
+                               const float* P, int B, int transposeP, const u32x4* gfrag, int mode,
+                               void* out, int out_f32, uint32_t* bits, int N, int M, hipStream_t s);
+
+// MFMA operand fragments of P for the forward permute and the block adjoint
+// (frag.hip): fwd [nb][frag_fwd_entries(B)], adj [nb][frag_adj_entries(B)].
+size_t frag_fwd_entries(int B);
+size_t frag_adj_entries(int B);
+hipError_t launch_frag(const float* P, const float* n, int nb, int B, u32x4* fwd, u32x4* adj,
+                       hipStream_t s);
 hipError_t launch_permute_f32(const float* A, int rows, int cin, const float* colscale,
                               const float* P, int B, int transposeP, int mode, float* out,
                               uint32_t* bits, int N, int M, hipStream_t s);
@@ -59,13 +76,16 @@ hipError_t launch_gemm_dd_f32(const float* R, int ldr, const float* X, int ldx, 
 hipError_t launch_error_finalize(const float* part, int nparts, float* E_ws, float* err,
                                  hipStream_t s);
 
-// Block adjoint (adjoint.hip): partial dP over row chunks.
-int adjoint_chunks(int cout, int nb, int B);
-hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const float* P,
-                               const uint32_t* bits, int cout, int cin, int B, int chunks,
+// Block adjoint (adjoint.hip). Workgroup g of the fixed grid takes tiles
+// [g*tpw, (g+1)*tpw) of the block-major 32-row tile sequence (tpb per block)
+// and writes one partial B x B matrix per block it touches to
+// part[(g * maxseg + (block - first block of g)) * B * B].
+AdjSplit adjoint_split(int cout, int cin, int B);
+hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const u32x4* gfrag, const float* P,
+                               const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
                                float* part, hipStream_t s);
 hipError_t launch_adjoint_f32(const float* G, const float* W, const float* P,
-                              const uint32_t* bits, int cout, int cin, int B, int chunks,
+                              const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
                               float* part, hipStream_t s);
 
 }  // namespace lcp

@@ -4,7 +4,7 @@
 // GEMM reads with the token index contiguous.
 //
 // Both kernels walk one strip of 64 channels down all T tokens, so each
-// column's sum of squares is accumulated by fixed threads in a fixed order
+// column's sum of squares is accumulated by fixed lanes in a fixed order
 // (deterministic, no atomics).
 #include "common.h"
 #include "kernels.h"
@@ -27,56 +27,99 @@ __global__ __launch_bounds__(256) void colnorm_f32_kernel(const float* __restric
   if (rg == 0 && c < cin) norms[c] = sqrtf((part[0][col] + part[1][col]) + (part[2][col] + part[3][col]));
 }
 
-// Tile of 64 tokens x 64 channels, bf16. Loads are 16-byte chunks, 8 per
-// token row; the transposed stores are 16-byte chunks of 8 tokens.
+// bf16: one workgroup per strip of 64 channels, 4 waves. Lane (cb, rb) of a
+// wave owns an 8 x 8 block (tokens 8rb.., channels 8cb..) of each 64 x 64
+// tile: it loads the 8 token rows (16 bytes each), transposes the block in
+// registers (one v_perm_b32 per output word) and stores the 8 channel rows
+// of Xt (16 bytes each), while summing squares for its 8 channels. Two tiles
+// are in flight per wave. Column sums are reduced across the 8 lanes of a
+// column block (shuffles) and the 4 waves (LDS) in a fixed order.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t wq[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = r[2 * p][c >> 1], b = r[2 * p + 1][c >> 1];
+      wq[p] = __builtin_amdgcn_perm(b, a, sel);
+    }
+    o[c] = u32x4{wq[0], wq[1], wq[2], wq[3]};
+  }
+}
+
 __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __restrict__ X,
                                                               int T, int cin, int pitch,
                                                               float* __restrict__ norms,
                                                               uint16_t* __restrict__ Xt) {
-  constexpr int LD = 64 + 8;  // padded row (uint16) of the LDS tile
-  __shared__ uint16_t tile[64 * LD];
   __shared__ float part[4][64];
-  const int t = threadIdx.x;
-  const int c0 = blockIdx.x * 64;
-  const int col = t & 63, rg = t >> 6;
-  float ss = 0.f;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  const int rb = l & 7, cb = l >> 3;
+  const int c0 = blockIdx.x * 64 + 8 * cb;          // this lane's 8 channels
+  const bool cok = c0 < cin;                         // cin % 8 == 0: all 8 or none
   const int t_end = Xt != nullptr ? pitch : T;
-  for (int t0 = 0; t0 < t_end; t0 += 64) {
+  float ss[8];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int id = t + 256 * q;
-      const int row = id >> 3, ch = id & 7;
-      const int gr = t0 + row, gc = c0 + ch * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gr < T && gc < cin) v = *reinterpret_cast<const u32x4*>(X + (size_t)gr * cin + gc);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * LD + ch * 8);
-      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  for (int c = 0; c < 8; ++c) ss[c] = 0.f;
+
+  auto load = [&](int t0, u32x4 (&r)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = t0 + 8 * rb + e;
+      r[e] = (cok && row < T) ? *reinterpret_cast<const u32x4*>(X + (size_t)row * cin + c0)
+                              : u32x4{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
+  };
+  auto consume = [&](int t0, const u32x4 (&r)[8]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float v = bf2f(tile[(rg * 16 + r) * LD + col]);
-      ss += v * v;
-    }
+    for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int id = t + 256 * q;
-      const int cc = id >> 3, tq = id & 7;
-      if (Xt != nullptr && c0 + cc < cin) {
-        u32x4 v;
-        v.x = tile[(8 * tq + 0) * LD + cc] | ((uint32_t)tile[(8 * tq + 1) * LD + cc] << 16);
-        v.y = tile[(8 * tq + 2) * LD + cc] | ((uint32_t)tile[(8 * tq + 3) * LD + cc] << 16);
-        v.z = tile[(8 * tq + 4) * LD + cc] | ((uint32_t)tile[(8 * tq + 5) * LD + cc] << 16);
-        v.w = tile[(8 * tq + 6) * LD + cc] | ((uint32_t)tile[(8 * tq + 7) * LD + cc] << 16);
-        *reinterpret_cast<u32x4*>(Xt + (size_t)(c0 + cc) * pitch + t0 + 8 * tq) = v;
+      for (int q = 0; q < 4; ++q) {
+        const float lo = lo_bf(r[e][q]), hi = hi_bf(r[e][q]);
+        ss[2 * q] = fmaf(lo, lo, ss[2 * q]);
+        ss[2 * q + 1] = fmaf(hi, hi, ss[2 * q + 1]);
       }
+    if (Xt != nullptr && cok) {
+      u32x4 o[8];
+      transpose8x8(r, o);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<u32x4*>(Xt + (size_t)(c0 + c) * pitch + t0 + 8 * rb) = o[c];
     }
-    __syncthreads();
+  };
+
+  // wave w covers token tiles w, w + 4, w + 8, ... (64 tokens each), two at a time
+  u32x4 ra[8], rb2[8];
+  int t0 = 64 * w;
+  for (; t0 + 256 < t_end; t0 += 512) {
+    load(t0, ra);
+    load(t0 + 256, rb2);
+    consume(t0, ra);
+    consume(t0 + 256, rb2);
   }
-  part[rg][col] = ss;
+  if (t0 < t_end) {
+    load(t0, ra);
+    consume(t0, ra);
+  }
+
+  // column sums: lanes rb = 0..7 of a column block, then the 4 waves
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float v = ss[c];
+    v += shfl_xor(v, 1);
+    v += shfl_xor(v, 2);
+    v += shfl_xor(v, 4);
+    ss[c] = v;
+  }
+  if (rb == 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) part[w][8 * cb + c] = ss[c];
+  }
   __syncthreads();
-  if (rg == 0 && c0 + col < cin)
-    norms[c0 + col] = sqrtf((part[0][col] + part[1][col]) + (part[2][col] + part[3][col]));
+  if (t < 64) {
+    const int c = blockIdx.x * 64 + t;
+    if (c < cin) norms[c] = sqrtf((part[0][t] + part[1][t]) + (part[2][t] + part[3][t]));
+  }
 }
 
 hipError_t launch_colnorm_f32(const float* X, int T, int cin, float* norms, hipStream_t s) {

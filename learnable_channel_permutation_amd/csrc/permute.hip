@@ -83,151 +83,169 @@ __device__ __forceinline__ void perm_prep(const float* __restrict__ P, const flo
   }
 }
 
+// Persistent grid: workgroup g takes the contiguous range of 32-row tiles
+// [g * tpw, (g + 1) * tpw) of the block-major tile sequence (tpb tiles per
+// block), so every workgroup gets the same amount of work and a range spans
+// at most a few blocks; the P fragments are (re)loaded into LDS when the
+// block changes. With `gfrag` the fragments come precomputed from global
+// memory (a coalesced copy), otherwise they are built here.
 template <int B, int MODE, int M>
 __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_kernel(
     const uint16_t* __restrict__ A, int rows, int cin, const float* __restrict__ colscale,
-    const float* __restrict__ P, int transposeP, int chunk_rows, void* __restrict__ out,
-    int out_f32, uint32_t* __restrict__ bits, int N) {
+    const float* __restrict__ P, int transposeP, const u32x4* __restrict__ gfrag, int tpw,
+    void* __restrict__ out, int out_f32, uint32_t* __restrict__ bits, int N) {
   using G = PermGeom<B, MODE>;
   constexpr int KS = G::KS, TT = G::TT;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  const int b = blockIdx.x;
-  perm_prep<B, MODE>(P, colscale, b, transposeP, lds);
-  __syncthreads();
-
   const u32x4* F1 = reinterpret_cast<const u32x4*>(lds);
   const u32x4* FQ = F1 + G::FRAG;
   const u32x4* F2 = F1 + (size_t)(1 + G::NSPLIT) * G::FRAG;
 
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int h = l >> 5, n = l & 31;
-  const int r0 = blockIdx.y * chunk_rows;
-  const int r1 = min(rows, r0 + chunk_rows);
-  const int colbase = b * B + 16 * h;
   const int words = cin >> 5;
+  const int tpb = (rows + 31) / 32;
+  const int total = (cin / B) * tpb;
+  const int t_begin = blockIdx.x * tpw;
+  const int t_end = min(total, t_begin + tpw);
 
-  u32x4 wop[KS];
-  auto load_tile = [&](int i0) {
-    const int i = i0 + n;
-#pragma unroll
-    for (int p = 0; p < KS; ++p) {
-      const int col = colbase + 32 * (p >> 1) + 8 * (p & 1);
-      if (i < r1) wop[p] = *reinterpret_cast<const u32x4*>(A + (size_t)i * cin + col);
-      else wop[p] = u32x4{0u, 0u, 0u, 0u};
+  for (int seg = t_begin; seg < t_end;) {
+    const int b = seg / tpb;
+    const int seg_end = min(t_end, (b + 1) * tpb);
+    __syncthreads();                      // previous block's fragments no longer read
+    if (gfrag != nullptr) {
+      const u32x4* src = gfrag + (size_t)b * G::NARR * G::FRAG;
+      u32x4* dst = reinterpret_cast<u32x4*>(lds);
+      for (int e = threadIdx.x; e < G::NARR * G::FRAG; e += G::THREADS) dst[e] = src[e];
+    } else {
+      perm_prep<B, MODE>(P, colscale, b, transposeP, lds);
     }
-  };
+    __syncthreads();
 
-  int i0 = r0 + 32 * w;
-  if (i0 < r1) load_tile(i0);
-  for (; i0 < r1; i0 += 32 * G::WAVES) {
-    // keep the P fragments in LDS: re-read them per tile instead of letting the
-    // compiler hoist all of them into registers (which caps occupancy at one
-    // wave per SIMD, or spills for B = 128)
-    __asm__ volatile("" ::: "memory");
-    const int i = i0 + n;
-    u32x4 cur[KS];
+    const int colbase = b * B + 16 * h;
+    u32x4 wop[KS];
+    auto load_tile = [&](int tile) {
+      const int i = (tile - b * tpb) * 32 + n;
 #pragma unroll
-    for (int p = 0; p < KS; ++p) cur[p] = wop[p];
-    if (i0 + 32 * G::WAVES < r1) load_tile(i0 + 32 * G::WAVES);   // prefetch the next tile
+      for (int p = 0; p < KS; ++p) {
+        const int col = colbase + 32 * (p >> 1) + 8 * (p & 1);
+        if (i < rows) wop[p] = *reinterpret_cast<const u32x4*>(A + (size_t)i * cin + col);
+        else wop[p] = u32x4{0u, 0u, 0u, 0u};
+      }
+    };
 
-    if (MODE == PERM_PLAIN) {
+    int tile = seg + w;
+    if (tile < seg_end) load_tile(tile);
+    for (; tile < seg_end; tile += G::WAVES) {
+      // keep the P fragments in LDS: re-read them per tile instead of letting
+      // the compiler hoist all of them into registers (which caps occupancy)
+      __asm__ volatile("" ::: "memory");
+      const int i = (tile - b * tpb) * 32 + n;
+      u32x4 cur[KS];
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        floatx16 acc = {};
+      for (int p = 0; p < KS; ++p) cur[p] = wop[p];
+      if (tile + G::WAVES < seg_end) load_tile(tile + G::WAVES);   // prefetch the next tile
+
+      if (MODE == PERM_PLAIN) {
 #pragma unroll
-        for (int p = 0; p < KS; ++p) acc = mfma32(F1[(t * KS + p) * 64 + l], cur[p], acc);
-        if (i < r1) {
-          const size_t o = (size_t)i * cin + colbase + 32 * t;
-          if (out_f32) {
-            floatx4* dst = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(out) + o);
+        for (int t = 0; t < TT; ++t) {
+          floatx16 acc = {};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dst[q] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-          } else {
-            u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + o);
+          for (int p = 0; p < KS; ++p) acc = mfma32(F1[(t * KS + p) * 64 + l], cur[p], acc);
+          if (i < rows) {
+            const size_t o = (size_t)i * cin + colbase + 32 * t;
+            if (out_f32) {
+              floatx4* dst = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(out) + o);
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-              dst[q] = u32x4{pack2(acc[8 * q], acc[8 * q + 1]), pack2(acc[8 * q + 2], acc[8 * q + 3]),
-                             pack2(acc[8 * q + 4], acc[8 * q + 5]), pack2(acc[8 * q + 6], acc[8 * q + 7])};
+              for (int q = 0; q < 4; ++q) dst[q] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            } else {
+              u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + o);
+#pragma unroll
+              for (int q = 0; q < 2; ++q)
+                dst[q] = u32x4{pack2(acc[8 * q], acc[8 * q + 1]), pack2(acc[8 * q + 2], acc[8 * q + 3]),
+                               pack2(acc[8 * q + 4], acc[8 * q + 5]), pack2(acc[8 * q + 6], acc[8 * q + 7])};
+            }
           }
         }
+        continue;
       }
-      continue;
-    }
 
-    u32x4 absw[KS];
+      u32x4 absw[KS];
 #pragma unroll
-    for (int p = 0; p < KS; ++p)
-      absw[p] = u32x4{cur[p].x & 0x7fff7fffu, cur[p].y & 0x7fff7fffu, cur[p].z & 0x7fff7fffu, cur[p].w & 0x7fff7fffu};
+      for (int p = 0; p < KS; ++p)
+        absw[p] = u32x4{cur[p].x & 0x7fff7fffu, cur[p].y & 0x7fff7fffu, cur[p].z & 0x7fff7fffu, cur[p].w & 0x7fff7fffu};
 
-    if (MODE == PERM_IMPORTANCE) {
+      if (MODE == PERM_IMPORTANCE) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          floatx16 acc = {};
+#pragma unroll
+          for (int s = G::NSPLIT - 1; s >= 0; --s)
+#pragma unroll
+            for (int p = 0; p < KS; ++p) acc = mfma32(FQ[(size_t)s * G::FRAG + (t * KS + p) * 64 + l], absw[p], acc);
+          if (i < rows) {
+            float* dst = reinterpret_cast<float*>(out) + (size_t)i * cin + colbase + 32 * t;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              reinterpret_cast<floatx4*>(dst)[q] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+          }
+        }
+        continue;
+      }
+
+      // ---- PERM_FWD: mask, A = W_hat . M, product 2, D = W - W_tilde
+      u32x4 aop[KS];
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        floatx16 acc = {};
+        floatx16 sh = {};
 #pragma unroll
         for (int s = G::NSPLIT - 1; s >= 0; --s)
 #pragma unroll
-          for (int p = 0; p < KS; ++p) acc = mfma32(FQ[(size_t)s * G::FRAG + (t * KS + p) * 64 + l], absw[p], acc);
-        if (i < r1) {
-          float* dst = reinterpret_cast<float*>(out) + (size_t)i * cin + colbase + 32 * t;
+          for (int p = 0; p < KS; ++p) sh = mfma32(FQ[(size_t)s * G::FRAG + (t * KS + p) * 64 + l], absw[p], sh);
+        float v[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            reinterpret_cast<floatx4*>(dst)[q] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-        }
-      }
-      continue;
-    }
+        for (int r = 0; r < 16; ++r) v[r] = nan_to_ninf(sh[r]);
+        uint32_t keep = 0;
+#pragma unroll
+        for (int g = 0; g < 16 / M; ++g) keep |= nm_keep<M>(v + g * M, N) << (g * M);
+        const uint32_t other = (uint32_t)__shfl_xor((int)keep, 32, 64);
+        if (h == 0 && i < rows) bits[(size_t)i * words + (b * B >> 5) + t] = keep | (other << 16);
 
-    // ---- PERM_FWD: mask, A = W_hat . M, product 2, D = W - W_tilde
-    u32x4 aop[KS];
+        floatx16 wh = {};
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      floatx16 sh = {};
-#pragma unroll
-      for (int s = G::NSPLIT - 1; s >= 0; --s)
-#pragma unroll
-        for (int p = 0; p < KS; ++p) sh = mfma32(FQ[(size_t)s * G::FRAG + (t * KS + p) * 64 + l], absw[p], sh);
-      float v[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = nan_to_ninf(sh[r]);
-      uint32_t keep = 0;
-#pragma unroll
-      for (int g = 0; g < 16 / M; ++g) keep |= nm_keep<M>(v + g * M, N) << (g * M);
-      const uint32_t other = (uint32_t)__shfl_xor((int)keep, 32, 64);
-      if (h == 0 && i < r1) bits[(size_t)i * words + (b * B >> 5) + t] = keep | (other << 16);
-
-      floatx16 wh = {};
-#pragma unroll
-      for (int p = 0; p < KS; ++p) wh = mfma32(F1[(t * KS + p) * 64 + l], cur[p], wh);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float a[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = ((keep >> (8 * u + e)) & 1u) ? wh[8 * u + e] : 0.f;
-        aop[2 * t + u] = u32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7])};
-      }
-    }
-#pragma unroll
-    for (int t2 = 0; t2 < TT; ++t2) {
-      floatx16 wt = {};
-#pragma unroll
-      for (int p2 = 0; p2 < KS; ++p2) wt = mfma32(F2[(t2 * KS + p2) * 64 + l], aop[p2], wt);
-      if (i < r1) {
-        u32x4 dv[2];
+        for (int p = 0; p < KS; ++p) wh = mfma32(F1[(t * KS + p) * 64 + l], cur[p], wh);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const u32x4 wv = cur[2 * t2 + u];
-          const uint32_t wq[4] = {wv.x, wv.y, wv.z, wv.w};
-          uint32_t d[4];
+          float a[8];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            d[q] = pack2(lo_bf(wq[q]) - wt[8 * u + 2 * q], hi_bf(wq[q]) - wt[8 * u + 2 * q + 1]);
-          dv[u] = u32x4{d[0], d[1], d[2], d[3]};
+          for (int e = 0; e < 8; ++e) a[e] = ((keep >> (8 * u + e)) & 1u) ? wh[8 * u + e] : 0.f;
+          aop[2 * t + u] = u32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7])};
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (size_t)i * cin + colbase + 32 * t2);
-        dst[0] = dv[0];
-        dst[1] = dv[1];
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < TT; ++t2) {
+        floatx16 wt = {};
+#pragma unroll
+        for (int p2 = 0; p2 < KS; ++p2) wt = mfma32(F2[(t2 * KS + p2) * 64 + l], aop[p2], wt);
+        if (i < rows) {
+          u32x4 dv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const u32x4 wv = cur[2 * t2 + u];
+            const uint32_t wq[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              d[q] = pack2(lo_bf(wq[q]) - wt[8 * u + 2 * q], hi_bf(wq[q]) - wt[8 * u + 2 * q + 1]);
+            dv[u] = u32x4{d[0], d[1], d[2], d[3]};
+          }
+          u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (size_t)i * cin + colbase + 32 * t2);
+          dst[0] = dv[0];
+          dst[1] = dv[1];
+        }
       }
     }
+    seg = seg_end;
   }
 }
 
@@ -308,53 +326,51 @@ __global__ __launch_bounds__(256) void diff_kernel(const void* __restrict__ W, c
 }
 
 // ---- launchers -------------------------------------------------------------------
-static int perm_chunk_rows(int rows, int nb) {
-  int chunks = (1024 + nb - 1) / nb;
-  if (chunks < 1) chunks = 1;
-  int cr = (rows + chunks - 1) / chunks;
-  cr = (cr + 255) / 256 * 256;
-  return cr;
-}
+// Fixed grid per block size (four resident workgroups per CU on 256 CUs for
+// B <= 64, one for B = 128), independent of the device, so the work split and
+// therefore every result is the same everywhere.
+static int perm_grid(int B) { return B == 128 ? 256 : 1024; }
 
 template <int B, int MODE, int M>
 static hipError_t perm_bf16_launch(const uint16_t* A, int rows, int cin, const float* colscale,
-                                   const float* P, int transposeP, void* out, int out_f32,
-                                   uint32_t* bits, int N, hipStream_t s) {
+                                   const float* P, int transposeP, const u32x4* gfrag, void* out,
+                                   int out_f32, uint32_t* bits, int N, hipStream_t s) {
   using G = PermGeom<B, MODE>;
-  const int nb = cin / B;
-  const int cr = perm_chunk_rows(rows, nb);
-  dim3 grid(nb, (rows + cr - 1) / cr);
+  const int total = (cin / B) * ((rows + 31) / 32);
+  int grid = perm_grid(B);
+  const int tpw = (total + grid - 1) / grid;
+  grid = (total + tpw - 1) / tpw;
   permute_bf16_kernel<B, MODE, M><<<grid, G::THREADS, G::LDS, s>>>(A, rows, cin, colscale, P, transposeP,
-                                                                    cr, out, out_f32, bits, N);
+                                                                    gfrag, tpw, out, out_f32, bits, N);
   return hipGetLastError();
 }
 
 template <int B, int MODE>
 static hipError_t perm_bf16_m(const uint16_t* A, int rows, int cin, const float* colscale, const float* P,
-                              int transposeP, void* out, int out_f32, uint32_t* bits, int N, int M,
-                              hipStream_t s) {
-  if (M == 8) return perm_bf16_launch<B, MODE, 8>(A, rows, cin, colscale, P, transposeP, out, out_f32, bits, N, s);
-  return perm_bf16_launch<B, MODE, 4>(A, rows, cin, colscale, P, transposeP, out, out_f32, bits, N, s);
+                              int transposeP, const u32x4* gfrag, void* out, int out_f32, uint32_t* bits,
+                              int N, int M, hipStream_t s) {
+  if (M == 8) return perm_bf16_launch<B, MODE, 8>(A, rows, cin, colscale, P, transposeP, gfrag, out, out_f32, bits, N, s);
+  return perm_bf16_launch<B, MODE, 4>(A, rows, cin, colscale, P, transposeP, gfrag, out, out_f32, bits, N, s);
 }
 
 template <int B>
 static hipError_t perm_bf16_b(const uint16_t* A, int rows, int cin, const float* colscale, const float* P,
-                              int transposeP, int mode, void* out, int out_f32, uint32_t* bits, int N,
-                              int M, hipStream_t s) {
+                              int transposeP, const u32x4* gfrag, int mode, void* out, int out_f32,
+                              uint32_t* bits, int N, int M, hipStream_t s) {
   switch (mode) {
-    case PERM_PLAIN: return perm_bf16_launch<B, PERM_PLAIN, 4>(A, rows, cin, colscale, P, transposeP, out, out_f32, bits, N, s);
-    case PERM_IMPORTANCE: return perm_bf16_launch<B, PERM_IMPORTANCE, 4>(A, rows, cin, colscale, P, transposeP, out, 1, bits, N, s);
-    default: return perm_bf16_m<B, PERM_FWD>(A, rows, cin, colscale, P, transposeP, out, 0, bits, N, M, s);
+    case PERM_PLAIN: return perm_bf16_launch<B, PERM_PLAIN, 4>(A, rows, cin, colscale, P, transposeP, nullptr, out, out_f32, bits, N, s);
+    case PERM_IMPORTANCE: return perm_bf16_launch<B, PERM_IMPORTANCE, 4>(A, rows, cin, colscale, P, transposeP, nullptr, out, 1, bits, N, s);
+    default: return perm_bf16_m<B, PERM_FWD>(A, rows, cin, colscale, P, transposeP, gfrag, out, 0, bits, N, M, s);
   }
 }
 
 hipError_t launch_permute_bf16(const uint16_t* A, int rows, int cin, const float* colscale,
-                               const float* P, int B, int transposeP, int mode, void* out,
-                               int out_f32, uint32_t* bits, int N, int M, hipStream_t s) {
+                               const float* P, int B, int transposeP, const u32x4* gfrag, int mode,
+                               void* out, int out_f32, uint32_t* bits, int N, int M, hipStream_t s) {
   switch (B) {
-    case 32: return perm_bf16_b<32>(A, rows, cin, colscale, P, transposeP, mode, out, out_f32, bits, N, M, s);
-    case 64: return perm_bf16_b<64>(A, rows, cin, colscale, P, transposeP, mode, out, out_f32, bits, N, M, s);
-    case 128: return perm_bf16_b<128>(A, rows, cin, colscale, P, transposeP, mode, out, out_f32, bits, N, M, s);
+    case 32: return perm_bf16_b<32>(A, rows, cin, colscale, P, transposeP, gfrag, mode, out, out_f32, bits, N, M, s);
+    case 64: return perm_bf16_b<64>(A, rows, cin, colscale, P, transposeP, gfrag, mode, out, out_f32, bits, N, M, s);
+    case 128: return perm_bf16_b<128>(A, rows, cin, colscale, P, transposeP, gfrag, mode, out, out_f32, bits, N, M, s);
   }
   return hipErrorInvalidValue;
 }

@@ -140,15 +140,17 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
 // (Gamma -= exp(U^i) . rowsum(Gamma)); dlogits = Gamma / tau. Z^i and U^i are
 // rebuilt from the logits and the offsets by the same sequence of
 // subtractions the forward performed, so they match it bit for bit.
-// dP is the sum of `parts` slices spaced `part_stride` floats apart (summed in
-// slice order). Offsets come from `off` ([nb][iters][2][B], as written by the
+// dP is dense [nb][B][B] (seg_tpw == 0) or the block adjoint's partials: the
+// workgroups g_lo..g_hi whose tile ranges cover block b each left one B x B
+// partial at slot g * maxseg + (b - first block of g); they are summed in
+// workgroup order. Offsets come from `off` ([nb][iters][2][B], as written by the
 // forward) or, when off == nullptr, are recomputed here. Dynamic LDS holds
 // 2 * iters * B floats.
 template <int B>
 __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
-    const float* __restrict__ logits, const float* __restrict__ dP, int parts, size_t part_stride,
-    const float* __restrict__ off, float* __restrict__ dlogits, int iters, float scale,
-    float inv_tau) {
+    const float* __restrict__ logits, const float* __restrict__ dP, int seg_tpw, int seg_tpb,
+    int seg_maxseg, int seg_grid, const float* __restrict__ off, float* __restrict__ dlogits, int iters,
+    float scale, float inv_tau) {
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
   extern __shared__ float sh_off[];          // [iters][2][B]
@@ -177,7 +179,11 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
   // rebuild Z^L and form Gamma = dP . exp(Z^L)
   float g[4][CPL];
   {
-    const float* dpb = dP + (size_t)b * B * B;
+    int g_lo = 0, g_hi = 0;
+    if (seg_tpw > 0) {
+      g_lo = (b * seg_tpb) / seg_tpw;
+      g_hi = min(seg_grid - 1, ((b + 1) * seg_tpb - 1) / seg_tpw);
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int row = 16 * w + 4 * lr + a;
@@ -189,8 +195,16 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
           v = v - sh_off[(2 * it) * B + row];
           v = v - sh_off[(2 * it + 1) * B + col];
         }
-        float d = 0.f;
-        for (int p = 0; p < parts; ++p) d += dpb[p * part_stride + row * B + col];
+        float d;
+        if (seg_tpw == 0) {
+          d = dP[(size_t)b * B * B + row * B + col];
+        } else {
+          d = 0.f;
+          for (int gg = g_lo; gg <= g_hi; ++gg) {
+            const int k = b - (gg * seg_tpw) / seg_tpb;
+            d += dP[((size_t)gg * seg_maxseg + k) * B * B + row * B + col];
+          }
+        }
         g[a][c] = d * exp2_(v);
       }
     }
@@ -280,16 +294,18 @@ hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb
   return hipGetLastError();
 }
 
-hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, int parts, size_t part_stride,
+hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, const AdjSplit* seg,
                                const float* off, float* dlogits, int nb, int B, int iters,
                                float tau, hipStream_t s) {
+  const int tpw = seg ? seg->tpw : 0, tpb = seg ? seg->tpb : 0;
+  const int maxseg = seg ? seg->maxseg : 0, grid = seg ? seg->grid : 0;
   const float scale = sk_scale(tau);
   const float inv_tau = (float)(1.0 / (double)tau);
   const size_t lds = (size_t)iters * 2 * B * sizeof(float);
   switch (B) {
-    case 32: sinkhorn_bwd_kernel<32><<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, dP, parts, part_stride, off, dlogits, iters, scale, inv_tau); break;
-    case 64: sinkhorn_bwd_kernel<64><<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, dP, parts, part_stride, off, dlogits, iters, scale, inv_tau); break;
-    case 128: sinkhorn_bwd_kernel<128><<<nb, SkGeom<128>::THREADS, lds, s>>>(logits, dP, parts, part_stride, off, dlogits, iters, scale, inv_tau); break;
+    case 32: sinkhorn_bwd_kernel<32><<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau); break;
+    case 64: sinkhorn_bwd_kernel<64><<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau); break;
+    case 128: sinkhorn_bwd_kernel<128><<<nb, SkGeom<128>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
