@@ -82,8 +82,7 @@ typedef struct lcp_cfg {
  * the step's stream immediately before (start[i]) and after (stop[i]) kernel i
  * of the step. NULL entries are skipped; a NULL lcp_timing* records nothing.
  * Forward kernels: 0 Sinkhorn, 1 permute+mask+unpermute, 2 error GEMM,
- * 3 error finalisation, 4 MFMA operand fragments of P (BF16 layers).
- * Backward kernels: 0 dD GEMM, 1 block adjoint, 2 Sinkhorn adjoint. */
+ * 3 error finalisation. Backward kernels: 0 dD GEMM, 1 block adjoint, 2 Sinkhorn adjoint. */
 typedef struct lcp_timing {
   void* start[8];
   void* stop[8];

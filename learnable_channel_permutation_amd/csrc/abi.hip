@@ -112,7 +112,7 @@ int lcp_sinkhorn(const float* logits, float* P, int nb, int B, int iters, float 
   if (!good_B(B)) return LCP_E_UNSUPPORTED;
   if ((long long)iters * B > kMaxIterB) return LCP_E_UNSUPPORTED;
   if (!fits_i32(nb, (long long)B * B) || !aligned16(logits) || !aligned16(P)) return LCP_E_INVAL;
-  LCP_RUN(launch_sinkhorn_fwd(logits, P, nullptr, nb, B, iters, tau, S(stream)));
+  LCP_RUN(launch_sinkhorn_fwd(logits, P, nullptr, nb, B, iters, tau, nullptr, nullptr, nullptr, S(stream)));
   return LCP_OK;
 }
 
@@ -258,13 +258,9 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
   u32x4* fragF = (u32x4*)(base + Ly.fragF);
   u32x4* fragA = (u32x4*)(base + Ly.fragA);
   tmr.start(0);
-  LCP_RUN(launch_sinkhorn_fwd(logits, P, off, Ly.nb, L->B, c->iters, c->tau, s));
+  LCP_RUN(launch_sinkhorn_fwd(logits, P, off, Ly.nb, L->B, c->iters, c->tau, L->norms, bf ? fragF : nullptr,
+                              bf ? fragA : nullptr, s));
   tmr.stop(0);
-  if (bf) {
-    tmr.start(4);
-    LCP_RUN(launch_frag(P, L->norms, Ly.nb, L->B, fragF, fragA, s));
-    tmr.stop(4);
-  }
   tmr.start(1);
   if (bf)
     LCP_RUN(launch_permute_bf16((const uint16_t*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, fragF, PERM_FWD,

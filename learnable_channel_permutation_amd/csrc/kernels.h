@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "frag.h"
 
 namespace lcp {
 
@@ -16,9 +17,12 @@ struct AdjSplit {
   int grid, tpw, tpb, maxseg;
 };
 
-// Sinkhorn (sinkhorn.hip)
+// Sinkhorn (sinkhorn.hip). With fwd != nullptr the forward also writes the
+// MFMA operand fragments of P (frag.h): fwd [nb][frag_fwd_entries(B)] from P
+// and the column norms n, adj [nb][frag_adj_entries(B)].
 hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb, int B,
-                               int iters, float tau, hipStream_t s);
+                               int iters, float tau, const float* n, u32x4* fwd, u32x4* adj,
+                               hipStream_t s);
 // dP is either dense [nb][B][B] (seg == nullptr) or the block adjoint's
 // (workgroup, segment) partials described by seg, summed in workgroup order.
 hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, const AdjSplit* seg,
@@ -40,17 +44,11 @@ enum PermMode {
   PERM_IMPORTANCE = 1,  // out = (|A| colscale) P_B, fp32, float32-accurate
   PERM_FWD = 2          // D = W - ((W P_B) . M) P_B^T and mask bits from (|W| n) P_B
 };
-// gfrag (nullable, forward mode only): precomputed fragments from launch_frag.
+// gfrag (nullable, forward mode only): precomputed fragments (frag.h).
 hipError_t launch_permute_bf16(const uint16_t* A, int rows, int cin, const float* colscale,
                                const float* P, int B, int transposeP, const u32x4* gfrag, int mode,
                                void* out, int out_f32, uint32_t* bits, int N, int M, hipStream_t s);
 
-// MFMA operand fragments of P for the forward permute and the block adjoint
-// (frag.hip): fwd [nb][frag_fwd_entries(B)], adj [nb][frag_adj_entries(B)].
-size_t frag_fwd_entries(int B);
-size_t frag_adj_entries(int B);
-hipError_t launch_frag(const float* P, const float* n, int nb, int B, u32x4* fwd, u32x4* adj,
-                       hipStream_t s);
 hipError_t launch_permute_f32(const float* A, int rows, int cin, const float* colscale,
                               const float* P, int B, int transposeP, int mode, float* out,
                               uint32_t* bits, int N, int M, hipStream_t s);

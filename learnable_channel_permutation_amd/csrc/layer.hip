@@ -27,13 +27,16 @@ __global__ __launch_bounds__(256) void colnorm_f32_kernel(const float* __restric
   if (rg == 0 && c < cin) norms[c] = sqrtf((part[0][col] + part[1][col]) + (part[2][col] + part[3][col]));
 }
 
-// bf16: one workgroup per strip of 64 channels, 4 waves. Lane (cb, rb) of a
-// wave owns an 8 x 8 block (tokens 8rb.., channels 8cb..) of each 64 x 64
-// tile: it loads the 8 token rows (16 bytes each), transposes the block in
-// registers (one v_perm_b32 per output word) and stores the 8 channel rows
-// of Xt (16 bytes each), while summing squares for its 8 channels. Two tiles
-// are in flight per wave. Column sums are reduced across the 8 lanes of a
-// column block (shuffles) and the 4 waves (LDS) in a fixed order.
+// bf16: one workgroup per strip of 32 channels, 4 waves; consecutive strips
+// go to the same XCD (workgroup ids are dealt round-robin over the 8 XCDs), so
+// the two 64-byte halves of a 128-byte row segment meet in one L2. Lane
+// (cb, rb) of a wave owns an 8 x 8 block (tokens 8rb.., channels 8cb..) of
+// each 128-token x 32-channel tile: it loads the 8 token rows (16 bytes
+// each), transposes the block in registers (one v_perm_b32 per output word)
+// and stores the 8 channel rows of Xt (16 bytes each), while summing squares
+// for its 8 channels. Two tiles are in flight per wave. Column sums are
+// reduced over the 16 lanes of a column block (one DPP row) and then over the
+// 4 waves (LDS), in a fixed order.
 __device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8]) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -52,10 +55,12 @@ __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __
                                                               int T, int cin, int pitch,
                                                               float* __restrict__ norms,
                                                               uint16_t* __restrict__ Xt) {
-  __shared__ float part[4][64];
+  __shared__ float part[4][32];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  const int rb = l & 7, cb = l >> 3;
-  const int c0 = blockIdx.x * 64 + 8 * cb;          // this lane's 8 channels
+  const int rb = l & 15, cb = l >> 4;
+  const int G = gridDim.x;
+  const int strip = ((G & 7) == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int c0 = strip * 32 + 8 * cb;               // this lane's 8 channels
   const bool cok = c0 < cin;                         // cin % 8 == 0: all 8 or none
   const int t_end = Xt != nullptr ? pitch : T;
   float ss[8];
@@ -79,7 +84,8 @@ __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __
         ss[2 * q] = fmaf(lo, lo, ss[2 * q]);
         ss[2 * q + 1] = fmaf(hi, hi, ss[2 * q + 1]);
       }
-    if (Xt != nullptr && cok) {
+    // pitch is a multiple of 64, so a group of 8 tokens is entirely inside or outside it
+    if (Xt != nullptr && cok && t0 + 8 * rb < pitch) {
       u32x4 o[8];
       transpose8x8(r, o);
 #pragma unroll
@@ -88,36 +94,30 @@ __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __
     }
   };
 
-  // wave w covers token tiles w, w + 4, w + 8, ... (64 tokens each), two at a time
+  // wave w covers token tiles w, w + 4, w + 8, ... (128 tokens each), two at a time
   u32x4 ra[8], rb2[8];
-  int t0 = 64 * w;
-  for (; t0 + 256 < t_end; t0 += 512) {
+  int t0 = 128 * w;
+  for (; t0 + 512 < t_end; t0 += 1024) {
     load(t0, ra);
-    load(t0 + 256, rb2);
+    load(t0 + 512, rb2);
     consume(t0, ra);
-    consume(t0 + 256, rb2);
+    consume(t0 + 512, rb2);
   }
   if (t0 < t_end) {
     load(t0, ra);
     consume(t0, ra);
   }
 
-  // column sums: lanes rb = 0..7 of a column block, then the 4 waves
+  // column sums: the 16 lanes rb of a column block (one DPP row), then the 4 waves
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float v = ss[c];
-    v += shfl_xor(v, 1);
-    v += shfl_xor(v, 2);
-    v += shfl_xor(v, 4);
-    ss[c] = v;
-  }
+  for (int c = 0; c < 8; ++c) ss[c] = row16_sum(ss[c]);
   if (rb == 0) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) part[w][8 * cb + c] = ss[c];
   }
   __syncthreads();
-  if (t < 64) {
-    const int c = blockIdx.x * 64 + t;
+  if (t < 32) {
+    const int c = strip * 32 + t;
     if (c < cin) norms[c] = sqrtf((part[0][t] + part[1][t]) + (part[2][t] + part[3][t]));
   }
 }
@@ -129,7 +129,7 @@ hipError_t launch_colnorm_f32(const float* X, int T, int cin, float* norms, hipS
 
 hipError_t launch_layer_init_bf16(const uint16_t* X, int T, int cin, int pitch, float* norms,
                                   uint16_t* Xt, hipStream_t s) {
-  layer_init_bf16_kernel<<<(cin + 63) / 64, 256, 0, s>>>(X, T, cin, pitch, norms, Xt);
+  layer_init_bf16_kernel<<<(cin + 31) / 32, 256, 0, s>>>(X, T, cin, pitch, norms, Xt);
   return hipGetLastError();
 }
 

@@ -326,10 +326,11 @@ __global__ __launch_bounds__(256) void diff_kernel(const void* __restrict__ W, c
 }
 
 // ---- launchers -------------------------------------------------------------------
-// Fixed grid per block size (four resident workgroups per CU on 256 CUs for
-// B <= 64, one for B = 128), independent of the device, so the work split and
-// therefore every result is the same everywhere.
-static int perm_grid(int B) { return B == 128 ? 256 : 1024; }
+// Grid: about one round of resident workgroups on 256 CUs (LDS and registers
+// allow 4 per CU for B = 32, 3 for B = 64 with the forward's six fragment
+// arrays, 1 for B = 128). Every tile is computed independently, so results do
+// not depend on the split.
+static int perm_grid(int B, int mode) { return B == 128 ? 256 : (B == 64 && mode == PERM_FWD) ? 768 : 1024; }
 
 template <int B, int MODE, int M>
 static hipError_t perm_bf16_launch(const uint16_t* A, int rows, int cin, const float* colscale,
@@ -337,7 +338,7 @@ static hipError_t perm_bf16_launch(const uint16_t* A, int rows, int cin, const f
                                    int out_f32, uint32_t* bits, int N, hipStream_t s) {
   using G = PermGeom<B, MODE>;
   const int total = (cin / B) * ((rows + 31) / 32);
-  int grid = perm_grid(B);
+  int grid = perm_grid(B, MODE);
   const int tpw = (total + grid - 1) / grid;
   grid = (total + tpw - 1) / tpw;
   permute_bf16_kernel<B, MODE, M><<<grid, G::THREADS, G::LDS, s>>>(A, rows, cin, colscale, P, transposeP,

@@ -10,10 +10,11 @@
 // 16w .. 16w+15; inside a wave lane l = 16*lr + lc holds rows 16w + 4lr + a
 // (a < 4) and columns lc*CPL + c (c < CPL = B/16), all in registers for every
 // iteration (no HBM or LDS round trip of the block). Row reductions run over
-// the 16 lanes of a lane row (xor 1, 2, 4, 8); column reductions over the 4
-// lane rows (xor 16, 32) and then across waves through LDS. Work is done in
-// base 2: z = logits * log2(e) / tau, lse2 = max + log2(sum exp2(z - max)), so
-// each normalisation costs one v_exp_f32 per element. The row offsets r_i and
+// the 16 lanes of a DPP row; column reductions pair lanes 16 and 32 apart
+// (permlane swaps) and then combine the waves' (max, sum) pairs through LDS
+// with one barrier per column step. Work is done in base 2:
+// z = logits * log2(e) / tau, lse2 = max + log2(sum exp2(z - max)), so each
+// normalisation costs one v_exp_f32 per element. The row offsets r_i and
 // column offsets c_i (base 2) are kept for the reverse pass.
 #include "common.h"
 #include "kernels.h"
@@ -27,29 +28,50 @@ struct SkGeom {
   static constexpr int CPL = B / 16;
 };
 
-// Load one block (times `scale`) into the lane's registers.
-template <int B>
-__device__ __forceinline__ void sk_load(const float* __restrict__ src, float scale,
-                                        float (&z)[4][SkGeom<B>::CPL], int w, int lr, int lc) {
-  constexpr int CPL = SkGeom<B>::CPL;
+// CPL consecutive floats (16-byte aligned for CPL >= 4, 8-byte for CPL = 2)
+template <int CPL>
+__device__ __forceinline__ void ld_cols(const float* p, float (&v)[CPL]) {
+  if constexpr (CPL % 4 == 0) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const float* p = src + (16 * w + 4 * lr + a) * B + lc * CPL;
+    for (int c = 0; c < CPL; c += 4) {
+      const floatx4 q = *reinterpret_cast<const floatx4*>(p + c);
+      v[c] = q[0]; v[c + 1] = q[1]; v[c + 2] = q[2]; v[c + 3] = q[3];
+    }
+  } else {
 #pragma unroll
     for (int c = 0; c < CPL; c += 2) {
-      float2 v = *reinterpret_cast<const float2*>(p + c);
-      z[a][c] = v.x * scale;
-      z[a][c + 1] = v.y * scale;
+      const float2 q = *reinterpret_cast<const float2*>(p + c);
+      v[c] = q.x; v[c + 1] = q.y;
     }
   }
 }
+template <int CPL>
+__device__ __forceinline__ void st_cols(float* p, const float (&v)[CPL]) {
+  if constexpr (CPL % 4 == 0) {
+#pragma unroll
+    for (int c = 0; c < CPL; c += 4) *reinterpret_cast<floatx4*>(p + c) = floatx4{v[c], v[c + 1], v[c + 2], v[c + 3]};
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; c += 2) *reinterpret_cast<float2*>(p + c) = float2{v[c], v[c + 1]};
+  }
+}
 
-// One forward iteration on the register block. Writes the row offsets of this
-// lane's rows to roff[row] (if lc == 0) and the column offsets to coff[col]
-// (if w == 0 && lr == 0); both pointers may be global or LDS (flat).
+// The lane's 4 x CPL elements of a row-major B x B block.
 template <int B>
-__device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float* red_m, float* red_s,
-                                        float* roff, float* coff, int w, int lr, int lc) {
+__device__ __forceinline__ void ld_block(const float* __restrict__ src, float (&v)[4][SkGeom<B>::CPL], int w,
+                                         int lr, int lc) {
+  constexpr int CPL = SkGeom<B>::CPL;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) ld_cols<CPL>(src + (16 * w + 4 * lr + a) * B + lc * CPL, v[a]);
+}
+
+// One forward iteration on the register block, using reduction buffer `red`
+// (WAVES * B (max, sum) pairs; alternate two buffers between iterations).
+// Writes the row offsets of this lane's rows to roff[row] (if lc == 0) and the
+// column offsets to coff[col] (if w == 0 && lr == 0); either may be null.
+template <int B>
+__device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* red, float* roff, float* coff,
+                                        int w, int lr, int lc) {
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
   // ---- row step: U = Z - lse_row(Z)
@@ -58,80 +80,88 @@ __device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float* re
     float m = z[a][0];
 #pragma unroll
     for (int c = 1; c < CPL; ++c) m = fmaxf(m, z[a][c]);
-#pragma unroll
-    for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, shfl_xor(m, x));
+    m = row16_max(m);
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s += exp2_(z[a][c] - m);
-#pragma unroll
-    for (int x = 1; x < 16; x <<= 1) s += shfl_xor(s, x);
+    s = row16_sum(s);
     const float r = m + log2_(s);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) z[a][c] -= r;
     if (roff != nullptr && lc == 0) roff[16 * w + 4 * lr + a] = r;
   }
-  // ---- column step: Z = U - lse_col(U)
-  float mc[CPL];
+  // ---- column step: Z = U - lse_col(U); each wave's (max, sum) over its 16 rows
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     float m = fmaxf(fmaxf(z[0][c], z[1][c]), fmaxf(z[2][c], z[3][c]));
-    m = fmaxf(m, shfl_xor(m, 16));
-    m = fmaxf(m, shfl_xor(m, 32));
-    if (lr == 0) red_m[w * B + lc * CPL + c] = m;
+    m = xor32_max(xor16_max(m));
+    float s = (exp2_(z[0][c] - m) + exp2_(z[1][c] - m)) + (exp2_(z[2][c] - m) + exp2_(z[3][c] - m));
+    s = xor32_sum(xor16_sum(s));
+    if (lr == 0) red[w * B + lc * CPL + c] = float2{m, s};
   }
   __syncthreads();
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    float m = red_m[lc * CPL + c];
+    const int col = lc * CPL + c;
+    float2 pv[WAVES];
 #pragma unroll
-    for (int v = 1; v < WAVES; ++v) m = fmaxf(m, red_m[v * B + lc * CPL + c]);
-    mc[c] = m;
-    float s = exp2_(z[0][c] - m) + exp2_(z[1][c] - m) + exp2_(z[2][c] - m) + exp2_(z[3][c] - m);
-    s += shfl_xor(s, 16);
-    s += shfl_xor(s, 32);
-    if (lr == 0) red_s[w * B + lc * CPL + c] = s;
-  }
-  __syncthreads();
+    for (int v = 0; v < WAVES; ++v) pv[v] = red[v * B + col];
+    float m = pv[0].x;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    float s = red_s[lc * CPL + c];
+    for (int v = 1; v < WAVES; ++v) m = fmaxf(m, pv[v].x);
+    float s = 0.f;
 #pragma unroll
-    for (int v = 1; v < WAVES; ++v) s += red_s[v * B + lc * CPL + c];
-    const float cc = mc[c] + log2_(s);
+    for (int v = 0; v < WAVES; ++v) s += pv[v].y * exp2_(pv[v].x - m);
+    const float cc = m + log2_(s);
 #pragma unroll
     for (int a = 0; a < 4; ++a) z[a][c] -= cc;
-    if (coff != nullptr && w == 0 && lr == 0) coff[lc * CPL + c] = cc;
+    if (coff != nullptr && w == 0 && lr == 0) coff[col] = cc;
   }
 }
 
 // Forward: P = exp2(Z^L); optional offsets off[b][i][0][row], off[b][i][1][col].
+// With fwd != nullptr the block of P and its column norms are staged in LDS
+// and the MFMA operand fragments (frag.h) are written as well.
 template <int B>
 __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
-    const float* __restrict__ logits, float* P, float* __restrict__ off, int iters, float scale) {
+    const float* __restrict__ logits, float* P, float* __restrict__ off, int iters, float scale,
+    const float* __restrict__ n, u32x4* __restrict__ fwd, u32x4* __restrict__ adj) {
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
-  __shared__ float red_m[WAVES * B];
-  __shared__ float red_s[WAVES * B];
+  constexpr int PP = B + 1;                       // LDS row pitch of the staged block
+  __shared__ float2 red[2][WAVES * B];
+  extern __shared__ float ps[];                   // [B][PP] P block, then [B] norms
   const int b = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l >> 4, lc = l & 15;
   float z[4][CPL];
-  sk_load<B>(logits + (size_t)b * B * B, scale, z, w, lr, lc);
+  ld_block<B>(logits + (size_t)b * B * B, z, w, lr, lc);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) z[a][c] *= scale;
   for (int it = 0; it < iters; ++it) {
     float* ro = off ? off + ((size_t)(b * iters + it) * 2 + 0) * B : nullptr;
     float* co = off ? off + ((size_t)(b * iters + it) * 2 + 1) * B : nullptr;
-    sk_iter<B>(z, red_m, red_s, ro, co, w, lr, lc);
+    sk_iter<B>(z, red[it & 1], ro, co, w, lr, lc);
   }
   float* dst = P + (size_t)b * B * B;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    float* p = dst + (16 * w + 4 * lr + a) * B + lc * CPL;
+    const int row = 16 * w + 4 * lr + a;
+    float v[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; c += 2) {
-      float2 v;
-      v.x = exp2_(z[a][c]);
-      v.y = exp2_(z[a][c + 1]);
-      *reinterpret_cast<float2*>(p + c) = v;
+    for (int c = 0; c < CPL; ++c) v[c] = exp2_(z[a][c]);
+    st_cols<CPL>(dst + row * B + lc * CPL, v);
+    if (fwd != nullptr) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ps[row * PP + lc * CPL + c] = v[c];
     }
+  }
+  if (fwd != nullptr) {
+    for (int i = t; i < B; i += SkGeom<B>::THREADS) ps[B * PP + i] = n[(size_t)b * B + i];
+    __syncthreads();
+    frag_build<B, PP>(ps, ps + B * PP, fwd + (size_t)b * FragGeom<B>::NARR * FragGeom<B>::FRAG,
+                      adj + (size_t)b * FragGeom<B>::FRAG, t, SkGeom<B>::THREADS);
   }
 }
 
@@ -143,7 +173,8 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
 // dP is dense [nb][B][B] (seg_tpw == 0) or the block adjoint's partials: the
 // workgroups g_lo..g_hi whose tile ranges cover block b each left one B x B
 // partial at slot g * maxseg + (b - first block of g); they are summed in
-// workgroup order. Offsets come from `off` ([nb][iters][2][B], as written by the
+// workgroup order, the loads of the next partial in flight while the current
+// one is added. Offsets come from `off` ([nb][iters][2][B], as written by the
 // forward) or, when off == nullptr, are recomputed here. Dynamic LDS holds
 // 2 * iters * B floats.
 template <int B>
@@ -154,17 +185,52 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
   extern __shared__ float sh_off[];          // [iters][2][B]
-  __shared__ float red_m[WAVES * B];
-  __shared__ float red_s[WAVES * B];
+  __shared__ float2 red[2][WAVES * B];
   __shared__ float red_g[2][WAVES * B];
   const int b = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l >> 4, lc = l & 15;
+  const int row0 = 16 * w + 4 * lr;          // this lane's rows row0 .. row0 + 3
 
   float z0[4][CPL];
-  sk_load<B>(logits + (size_t)b * B * B, scale, z0, w, lr, lc);
+  ld_block<B>(logits + (size_t)b * B * B, z0, w, lr, lc);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) z0[a][c] *= scale;
+
+  // dP of this block: dense, or the sum of the adjoint's partials
+  float d[4][CPL];
+  if (seg_tpw == 0) {
+    ld_block<B>(dP + (size_t)b * B * B, d, w, lr, lc);
+  } else {
+    const int g_lo = (b * seg_tpb) / seg_tpw;
+    const int g_hi = min(seg_grid - 1, ((b + 1) * seg_tpb - 1) / seg_tpw);
+    auto slot = [&](int gg) {
+      return dP + ((size_t)gg * seg_maxseg + (b - (gg * seg_tpw) / seg_tpb)) * B * B;
+    };
+    float cur[4][CPL];
+    ld_block<B>(slot(g_lo), cur, w, lr, lc);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) d[a][c] = 0.f;
+    for (int gg = g_lo; gg <= g_hi; ++gg) {
+      float nxt[4][CPL];
+      if (gg < g_hi) ld_block<B>(slot(gg + 1), nxt, w, lr, lc);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          d[a][c] += cur[a][c];
+          cur[a][c] = (gg < g_hi) ? nxt[a][c] : 0.f;
+        }
+    }
+  }
+
   if (off != nullptr) {
     const float* src = off + (size_t)b * iters * 2 * B;
-    for (int i = t; i < iters * 2 * B; i += SkGeom<B>::THREADS) sh_off[i] = src[i];
+    for (int i = 4 * t; i < iters * 2 * B; i += 4 * SkGeom<B>::THREADS)
+      *reinterpret_cast<floatx4*>(sh_off + i) = *reinterpret_cast<const floatx4*>(src + i);
   } else {
     float z[4][CPL];
 #pragma unroll
@@ -172,94 +238,80 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
 #pragma unroll
       for (int c = 0; c < CPL; ++c) z[a][c] = z0[a][c];
     for (int it = 0; it < iters; ++it)
-      sk_iter<B>(z, red_m, red_s, sh_off + (2 * it) * B, sh_off + (2 * it + 1) * B, w, lr, lc);
+      sk_iter<B>(z, red[it & 1], sh_off + (2 * it) * B, sh_off + (2 * it + 1) * B, w, lr, lc);
   }
   __syncthreads();
 
-  // rebuild Z^L and form Gamma = dP . exp(Z^L)
+  // Z^k for this lane's elements: z0 minus the offsets of iterations < k, in
+  // the forward's order (row offset, then column offset, per iteration)
+  auto rebuild = [&](int k, float (&v)[4][CPL]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[a][c] = z0[a][c];
+    for (int i = 0; i < k; ++i) {
+      const floatx4 r = *reinterpret_cast<const floatx4*>(sh_off + (2 * i) * B + row0);
+      float cv[CPL];
+      ld_cols<CPL>(sh_off + (2 * i + 1) * B + lc * CPL, cv);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[a][c] = (v[a][c] - r[a]) - cv[c];
+    }
+  };
+
   float g[4][CPL];
   {
-    int g_lo = 0, g_hi = 0;
-    if (seg_tpw > 0) {
-      g_lo = (b * seg_tpb) / seg_tpw;
-      g_hi = min(seg_grid - 1, ((b + 1) * seg_tpb - 1) / seg_tpw);
-    }
+    float v[4][CPL];
+    rebuild(iters, v);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int row = 16 * w + 4 * lr + a;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int col = lc * CPL + c;
-        float v = z0[a][c];
-        for (int it = 0; it < iters; ++it) {
-          v = v - sh_off[(2 * it) * B + row];
-          v = v - sh_off[(2 * it + 1) * B + col];
-        }
-        float d;
-        if (seg_tpw == 0) {
-          d = dP[(size_t)b * B * B + row * B + col];
-        } else {
-          d = 0.f;
-          for (int gg = g_lo; gg <= g_hi; ++gg) {
-            const int k = b - (gg * seg_tpw) / seg_tpb;
-            d += dP[((size_t)gg * seg_maxseg + k) * B * B + row * B + col];
-          }
-        }
-        g[a][c] = d * exp2_(v);
-      }
-    }
+      for (int c = 0; c < CPL; ++c) g[a][c] = d[a][c] * exp2_(v[a][c]);
   }
 
   for (int it = iters - 1; it >= 0; --it) {
-    float* red = red_g[it & 1];
-    // exp(U^i) and exp(Z^i) for this iteration
+    float* rg = red_g[it & 1];
+    // exp(U^i) and exp(Z^i) of this iteration
     float eu[4][CPL], ez[4][CPL];
+    {
+      float v[4][CPL];
+      rebuild(it, v);
+      const floatx4 r = *reinterpret_cast<const floatx4*>(sh_off + (2 * it) * B + row0);
+      float cv[CPL];
+      ld_cols<CPL>(sh_off + (2 * it + 1) * B + lc * CPL, cv);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int row = 16 * w + 4 * lr + a;
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int col = lc * CPL + c;
-        float v = z0[a][c];
-        for (int k = 0; k < it; ++k) {
-          v = v - sh_off[(2 * k) * B + row];
-          v = v - sh_off[(2 * k + 1) * B + col];
+        for (int c = 0; c < CPL; ++c) {
+          const float u = v[a][c] - r[a];
+          eu[a][c] = exp2_(u);
+          ez[a][c] = exp2_(u - cv[c]);
         }
-        const float u = v - sh_off[(2 * it) * B + row];
-        const float zz = u - sh_off[(2 * it + 1) * B + col];
-        eu[a][c] = exp2_(u);
-        ez[a][c] = exp2_(zz);
-      }
     }
-    // undo the column step: column sums of Gamma
-    float cs[CPL];
+    // undo the column step: column sums of Gamma over the 4 lane rows, then the waves
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       float s = (g[0][c] + g[1][c]) + (g[2][c] + g[3][c]);
-      s += shfl_xor(s, 16);
-      s += shfl_xor(s, 32);
-      if (lr == 0) red[w * B + lc * CPL + c] = s;
+      s = xor32_sum(xor16_sum(s));
+      if (lr == 0) rg[w * B + lc * CPL + c] = s;
     }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      float s = red[lc * CPL + c];
+      float s = rg[lc * CPL + c];
 #pragma unroll
-      for (int v = 1; v < WAVES; ++v) s += red[v * B + lc * CPL + c];
-      cs[c] = s;
+      for (int v = 1; v < WAVES; ++v) s += rg[v * B + lc * CPL + c];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) g[a][c] -= ez[a][c] * s;
     }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) g[a][c] -= ez[a][c] * cs[c];
     // undo the row step: row sums of Gamma (within the wave)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       float s = 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) s += g[a][c];
-#pragma unroll
-      for (int x = 1; x < 16; x <<= 1) s += shfl_xor(s, x);
+      s = row16_sum(s);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) g[a][c] -= eu[a][c] * s;
     }
@@ -268,14 +320,10 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
   float* dst = dlogits + (size_t)b * B * B;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    float* p = dst + (16 * w + 4 * lr + a) * B + lc * CPL;
+    float v[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; c += 2) {
-      float2 v;
-      v.x = g[a][c] * inv_tau;
-      v.y = g[a][c + 1] * inv_tau;
-      *reinterpret_cast<float2*>(p + c) = v;
-    }
+    for (int c = 0; c < CPL; ++c) v[c] = g[a][c] * inv_tau;
+    st_cols<CPL>(dst + (row0 + a) * B + lc * CPL, v);
   }
 }
 
@@ -283,12 +331,14 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
 static inline float sk_scale(float tau) { return (float)(1.4426950408889634 / (double)tau); }
 
 hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb, int B,
-                               int iters, float tau, hipStream_t s) {
+                               int iters, float tau, const float* n, u32x4* fwd, u32x4* adj,
+                               hipStream_t s) {
   const float scale = sk_scale(tau);
+  const size_t lds = fwd ? (size_t)(B * (B + 1) + B) * sizeof(float) : 0;
   switch (B) {
-    case 32: sinkhorn_fwd_kernel<32><<<nb, SkGeom<32>::THREADS, 0, s>>>(logits, P, off, iters, scale); break;
-    case 64: sinkhorn_fwd_kernel<64><<<nb, SkGeom<64>::THREADS, 0, s>>>(logits, P, off, iters, scale); break;
-    case 128: sinkhorn_fwd_kernel<128><<<nb, SkGeom<128>::THREADS, 0, s>>>(logits, P, off, iters, scale); break;
+    case 32: sinkhorn_fwd_kernel<32><<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
+    case 64: sinkhorn_fwd_kernel<64><<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
+    case 128: sinkhorn_fwd_kernel<128><<<nb, SkGeom<128>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
