@@ -282,8 +282,7 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
   tmr.stop(3);
   if (P_out)
     LCP_RUN(hipMemcpyAsync(P_out, P, (size_t)Ly.nb * L->B * L->B * 4, hipMemcpyDeviceToDevice, s));
-  if (bits_out)
-    LCP_RUN(hipMemcpyAsync(bits_out, bits, (size_t)L->cout * (L->cin / 32) * 4, hipMemcpyDeviceToDevice, s));
+  if (bits_out) LCP_RUN(launch_bits_rowmajor(bits, L->cout, L->cin, L->B, bits_out, s));
   return LCP_OK;
 }
 

@@ -85,7 +85,6 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
   const int h = l >> 5, n = l & 31;
   const int slot = w / WS;          // row tile slot of this wave
   const int half = w % WS;          // column blocks t2 = half * OWN + o
-  const int words = cin >> 5;
   unsigned char* ring = rings + slot * S * STAGE;
   const u32x4* F = reinterpret_cast<const u32x4*>(fb);
   const int lrow = remap_row(n);    // tile row whose operands this lane fetches
@@ -137,13 +136,14 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
         __builtin_amdgcn_global_load_lds(sw, (adj_lds_t)(sb + p * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(sg, (adj_lds_t)(sb + (KS + p) * 1024), 16, 0, 0);
       }
-      // mask words: instruction q, lane (h, n) -> word 2q + h of row i0 + n
+      // mask words (block-major [block][row][TT]): instruction q, lane (h, n)
+      // -> word 2q + h of row i0 + n, all inside the tile's 32 * TT words
 #pragma unroll
       for (int q = 0; q < Gm::BI; ++q) {
         if (q % WS != half) continue;
         const int a = (2 * q + h) % TT;
         const int ib = i0 + n;
-        const void* sbits = (ib < cout) ? (const void*)(bits + (size_t)ib * words + ((b * B) >> 5) + a)
+        const void* sbits = (ib < cout) ? (const void*)(bits + ((size_t)b * cout + ib) * TT + a)
                                         : (const void*)g_adj_zero;
         __builtin_amdgcn_global_load_lds(sbits, (adj_lds_t)(sb + 2 * KS * 1024 + q * 256), 4, 0, 0);
       }
@@ -291,7 +291,6 @@ __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restric
   __shared__ float pb[B][B + 1];
   __shared__ float wr[B], gr[B], am[B], ym[B];
   const int t = threadIdx.x;
-  const int words = cin >> 5;
   const int tpb = (cout + 31) / 32;
   const int total = (cin / B) * tpb;
   const int t_begin = blockIdx.x * tpw;
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restric
           s1 = fmaf(wr[j], pb[j][t], s1);
           s2 = fmaf(gr[j], pb[j][t], s2);
         }
-        const uint32_t keep = (bits[(size_t)i * words + ((b * B + t) >> 5)] >> (t & 31)) & 1u;
+        const uint32_t keep = (bits[((size_t)b * cout + i) * (B >> 5) + (t >> 5)] >> (t & 31)) & 1u;
         am[t] = keep ? s1 : 0.f;
         ym[t] = keep ? s2 : 0.f;
       }

@@ -37,6 +37,9 @@ hipError_t launch_layer_init_bf16(const uint16_t* X, int T, int cin, int pitch, 
 // N:M mask from fp32 scores (mask.hip).
 hipError_t launch_nm_mask(const float* scores, int rows, int cin, int N, int M, uint32_t* bits,
                           hipStream_t s);
+// The step keeps its mask block-major, [nb][rows][B / 32] words, so that a
+// 32-row tile's words are contiguous; this converts to [rows][cin / 32].
+hipError_t launch_bits_rowmajor(const uint32_t* bm, int rows, int cin, int B, uint32_t* out, hipStream_t s);
 
 // Block permutation kernels (permute.hip).
 enum PermMode {

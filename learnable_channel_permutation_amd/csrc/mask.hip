@@ -39,4 +39,22 @@ hipError_t launch_nm_mask(const float* scores, int rows, int cin, int N, int M, 
   return hipGetLastError();
 }
 
+// Mask words of the step (block-major: word a of row i in block b at
+// (b * rows + i) * (B / 32) + a) to the row-major layout [rows][cin / 32].
+__global__ __launch_bounds__(256) void bits_rowmajor_kernel(const uint32_t* __restrict__ bm, int rows,
+                                                            int words, int tt, uint32_t* __restrict__ out) {
+  const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long long)rows * words) return;
+  const int i = (int)(id / words), wd = (int)(id % words);
+  const int b = wd / tt, a = wd % tt;
+  out[id] = bm[((size_t)b * rows + i) * tt + a];
+}
+
+hipError_t launch_bits_rowmajor(const uint32_t* bm, int rows, int cin, int B, uint32_t* out, hipStream_t s) {
+  const int words = cin / 32;
+  const long long n = (long long)rows * words;
+  bits_rowmajor_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(bm, rows, words, B / 32, out);
+  return hipGetLastError();
+}
+
 }  // namespace lcp

@@ -103,7 +103,6 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
 
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int h = l >> 5, n = l & 31;
-  const int words = cin >> 5;
   const int tpb = (rows + 31) / 32;
   const int total = (cin / B) * tpb;
   const int t_begin = blockIdx.x * tpw;
@@ -195,6 +194,7 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
 
       // ---- PERM_FWD: mask, A = W_hat . M, product 2, D = W - W_tilde
       u32x4 aop[KS];
+      uint32_t kw[TT];
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         floatx16 sh = {};
@@ -209,7 +209,7 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
 #pragma unroll
         for (int g = 0; g < 16 / M; ++g) keep |= nm_keep<M>(v + g * M, N) << (g * M);
         const uint32_t other = (uint32_t)__shfl_xor((int)keep, 32, 64);
-        if (h == 0 && i < rows) bits[(size_t)i * words + (b * B >> 5) + t] = keep | (other << 16);
+        kw[t] = keep | (other << 16);
 
         floatx16 wh = {};
 #pragma unroll
@@ -221,6 +221,13 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
           for (int e = 0; e < 8; ++e) a[e] = ((keep >> (8 * u + e)) & 1u) ? wh[8 * u + e] : 0.f;
           aop[2 * t + u] = u32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7])};
         }
+      }
+      // mask words, block-major: the tile's 32 rows x TT words are contiguous
+      if (h == 0 && i < rows) {
+        uint32_t* bw = bits + ((size_t)b * rows + i) * TT;
+        if constexpr (TT == 4) *reinterpret_cast<u32x4*>(bw) = u32x4{kw[0], kw[1], kw[2], kw[3]};
+        else if constexpr (TT == 2) *reinterpret_cast<uint2*>(bw) = uint2{kw[0], kw[1]};
+        else bw[0] = kw[0];
       }
 #pragma unroll
       for (int t2 = 0; t2 < TT; ++t2) {
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(256) void permute_f32_kernel(const float* __restric
     for (int e = 0; e < 32; ++e) v[e] = nan_to_ninf(shat[rr][32 * q + e]);
     for (int g = 0; g < 32 / M; ++g) wbits |= nm_keep<M>(v + g * M, N) << (g * M);
     kw[rr][q] = wbits;
-    if (i < rows) bits[(size_t)i * (cin >> 5) + (b * B >> 5) + q] = wbits;
+    if (i < rows) bits[((size_t)b * rows + i) * (B >> 5) + q] = wbits;
   }
   __syncthreads();
   for (int k = q; k < B; k += 32)
