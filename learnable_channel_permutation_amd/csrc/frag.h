@@ -25,50 +25,82 @@ struct FragGeom {
   static constexpr int NARR = 2 + NSPLIT;          // F1, FQ[NSPLIT], F2
 };
 
-// Ps: P_b in LDS with row pitch PP floats; ns: the block's B norms in LDS.
-// Threads tid = 0 .. nthr-1 of the workgroup share the entries.
+// Eight floats -> one 16-byte entry of bf16, round to nearest even
+// (v_cvt_pk_bf16_f32); split terms are exact in bf16 and convert unchanged.
+__device__ __forceinline__ u32x4 pack8(const float (&v)[8]) {
+  return u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+}
+__device__ __forceinline__ void unpack8(const u32x4& w, float (&v)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = lo_bf(w[q]);
+    v[2 * q + 1] = hi_bf(w[q]);
+  }
+}
+
+// Ps: P_b in LDS with row pitch PP floats (PP even); ns: the block's B norms
+// in LDS. Threads tid = 0 .. nthr-1 of the workgroup share the entries; each
+// entry index yields one entry of every array (the FQ terms of an entry come
+// from one split of the same eight products).
 template <int B, int PP>
 __device__ __forceinline__ void frag_build(const float* Ps, const float* ns, u32x4* __restrict__ fo,
                                            u32x4* __restrict__ ao, int tid, int nthr) {
   using G = FragGeom<B>;
   constexpr int KS = G::KS, FRAG = G::FRAG, NSPLIT = G::NSPLIT;
-  for (int id = tid; id < (G::NARR + 1) * FRAG; id += nthr) {
-    const int arr = id / FRAG, ent = id % FRAG;
+  static_assert(PP % 2 == 0, "F2 rows are read as float2");
+  for (int ent = tid; ent < FRAG; ent += nthr) {
     const int lane = ent & 63, tp = ent >> 6;          // tp = t * KS + p
     const int t = tp / KS, p = tp % KS;
     const int h = lane >> 5, rho = lane & 31;
-    float v[8];
-    if (arr < 1 + NSPLIT) {                            // F1 or FQ[arr - 1]
+    const int half = 16 * h + 8 * (p & 1);
+    // F1 and FQ: row k = 32t + remap(rho), K = source channels jb .. jb + 7
+    {
       const int k = 32 * t + remap_row(rho);
-      const int jb = 32 * (p >> 1) + 16 * h + 8 * (p & 1);
+      const int jb = 32 * (p >> 1) + half;
+      float pv[8], q[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pv = Ps[(jb + e) * PP + k];
-        if (arr == 0) {
-          v[e] = pv;
-        } else {
-          const float q = ns[jb + e] * pv;
-          const float hi = bf2f(f2bf(q));
-          const float r1 = q - hi;
-          const float mid = bf2f(f2bf(r1));
-          v[e] = (arr == 1) ? hi : (arr == 2) ? mid : (r1 - mid);
-        }
+        pv[e] = Ps[(jb + e) * PP + k];
+        q[e] = ns[jb + e] * pv[e];
       }
-    } else if (arr == 1 + NSPLIT) {                    // F2
-      const int j = 32 * t + remap_row(rho);
-      const int kb = 32 * (p >> 1) + 16 * h + 8 * (p & 1);
+      fo[ent] = pack8(pv);
+      const u32x4 hi = pack8(q);
+      float hv[8], r[8];
+      unpack8(hi, hv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = Ps[j * PP + kb + e];
-    } else {                                           // FB (adjoint)
+      for (int e = 0; e < 8; ++e) r[e] = q[e] - hv[e];     // exact
+      const u32x4 mid = pack8(r);
+      fo[FRAG + ent] = hi;
+      fo[2 * FRAG + ent] = mid;
+      if (NSPLIT > 2) {
+        float mv[8], lo[8];
+        unpack8(mid, mv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = r[e] - mv[e];  // exact, a bf16 value
+        fo[3 * FRAG + ent] = pack8(lo);
+      }
+    }
+    // F2: row j = 32t + remap(rho), K = positions kb .. kb + 7 (contiguous in a row)
+    {
+      const int j = 32 * t + remap_row(rho);
+      const int kb = 32 * (p >> 1) + half;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float2 x = *reinterpret_cast<const float2*>(Ps + j * PP + kb + e);
+        v[e] = x.x;
+        v[e + 1] = x.y;
+      }
+      fo[(1 + NSPLIT) * FRAG + ent] = pack8(v);
+    }
+    // FB (adjoint): Pb[16p + 8h + e][32t + rho]
+    {
       const int k = 32 * t + rho;
+      float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = Ps[(16 * p + 8 * h + e) * PP + k];
+      ao[ent] = pack8(v);
     }
-    // the split terms are exact bf16 values; the others round to nearest even
-    const u32x4 o = {f2bf(v[0]) | (f2bf(v[1]) << 16), f2bf(v[2]) | (f2bf(v[3]) << 16),
-                     f2bf(v[4]) | (f2bf(v[5]) << 16), f2bf(v[6]) | (f2bf(v[7]) << 16)};
-    if (arr <= 1 + NSPLIT) fo[arr * FRAG + ent] = o;
-    else ao[ent] = o;
   }
 }
 

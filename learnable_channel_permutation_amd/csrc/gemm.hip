@@ -265,21 +265,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-// E = sqrt(sum of partials), summed in a fixed order by one workgroup.
-__global__ __launch_bounds__(256) void error_finalize_kernel(const float* __restrict__ part, int n,
-                                                             float* __restrict__ E_ws,
-                                                             float* __restrict__ err) {
-  __shared__ float red[256];
+// E = sqrt(sum of partials), summed in a fixed order by one wave: lane l adds
+// part[l], part[l + 64], ... in order, then the lanes are combined by a fixed
+// butterfly.
+__global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restrict__ part, int n,
+                                                            float* __restrict__ E_ws,
+                                                            float* __restrict__ err) {
   float s = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) s += part[i];
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int k = 128; k >= 1; k >>= 1) {
-    if ((int)threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
-    __syncthreads();
-  }
+  for (int i = threadIdx.x; i < n; i += 64) s += part[i];
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) s += shfl_xor(s, x);
   if (threadIdx.x == 0) {
-    const float E = sqrtf(red[0]);
+    const float E = sqrtf(s);
     if (E_ws) *E_ws = E;
     if (err) *err = E;
   }
@@ -329,7 +326,7 @@ hipError_t launch_gemm_dd_f32(const float* R, int ldr, const float* X, int ldx, 
 
 hipError_t launch_error_finalize(const float* part, int nparts, float* E_ws, float* err,
                                  hipStream_t s) {
-  error_finalize_kernel<<<1, 256, 0, s>>>(part, nparts, E_ws, err);
+  error_finalize_kernel<<<1, 64, 0, s>>>(part, nparts, E_ws, err);
   return hipGetLastError();
 }
 

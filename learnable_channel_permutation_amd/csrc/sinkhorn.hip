@@ -128,7 +128,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
     const float* __restrict__ n, u32x4* __restrict__ fwd, u32x4* __restrict__ adj) {
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
-  constexpr int PP = B + 1;                       // LDS row pitch of the staged block
+  constexpr int PP = B + 2;                       // LDS row pitch of the staged block
   __shared__ float2 red[2][WAVES * B];
   extern __shared__ float ps[];                   // [B][PP] P block, then [B] norms
   const int b = blockIdx.x;
@@ -334,7 +334,7 @@ hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb
                                int iters, float tau, const float* n, u32x4* fwd, u32x4* adj,
                                hipStream_t s) {
   const float scale = sk_scale(tau);
-  const size_t lds = fwd ? (size_t)(B * (B + 1) + B) * sizeof(float) : 0;
+  const size_t lds = fwd ? (size_t)(B * (B + 2) + B) * sizeof(float) : 0;
   switch (B) {
     case 32: sinkhorn_fwd_kernel<32><<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
     case 64: sinkhorn_fwd_kernel<64><<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
