@@ -26,6 +26,11 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file extra flags. permute.hip does VALU work on every MFMA result; the
+# VGPR form of MFMA keeps the accumulators out of AGPRs (no copy-out).
+FILE_FLAGS = {"permute.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc():
     for cand in ("/opt/rocm/bin/hipcc", "hipcc"):
         if os.path.isabs(cand) and os.path.exists(cand):
@@ -39,7 +44,7 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    cmd = [_hipcc()] + HIPCC_FLAGS + ["-c", src, "-o", obj]
+    cmd = [_hipcc()] + HIPCC_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, p.stderr))

@@ -90,6 +90,39 @@ __device__ __forceinline__ uint32_t nm_keep(const float* v, int N) {
   return bits;
 }
 
+// M = 4 with N fixed at compile time, for scores that cannot be -inf (sums
+// of non-negative products: every value is in [+0, +inf] or NaN). Same rule
+// as nm_keep with NaN read as -inf: for j < k, j outranks k iff
+// v_j >= v_k or v_k is NaN (a NaN v_j cannot reach a finite v_k, and no
+// v_k is -inf). The comparisons become wave-wide 64-bit ballots; beats[k]
+// lists the three events "another position outranks k", k is kept iff fewer
+// than N of them hold, evaluated with scalar 64-bit and/or/not, and
+// inverse_ballot hands each lane its own bit back as a condition. Every lane
+// of the wave must be active.
+template <int N>
+__device__ __forceinline__ void nm_keep4_nonneg(const float* v, bool* keep) {
+  typedef unsigned long long u64;
+  const u64 n1 = __builtin_amdgcn_ballot_w64(__builtin_isnan(v[1]));
+  const u64 n2 = __builtin_amdgcn_ballot_w64(__builtin_isnan(v[2]));
+  const u64 n3 = __builtin_amdgcn_ballot_w64(__builtin_isnan(v[3]));
+  const u64 c01 = __builtin_amdgcn_ballot_w64(v[0] >= v[1]) | n1;
+  const u64 c02 = __builtin_amdgcn_ballot_w64(v[0] >= v[2]) | n2;
+  const u64 c03 = __builtin_amdgcn_ballot_w64(v[0] >= v[3]) | n3;
+  const u64 c12 = __builtin_amdgcn_ballot_w64(v[1] >= v[2]) | n2;
+  const u64 c13 = __builtin_amdgcn_ballot_w64(v[1] >= v[3]) | n3;
+  const u64 c23 = __builtin_amdgcn_ballot_w64(v[2] >= v[3]) | n3;
+  const u64 beats[4][3] = {{~c01, ~c02, ~c03}, {c01, ~c12, ~c13}, {c02, c12, ~c23}, {c03, c13, c23}};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const u64 x = beats[k][0], y = beats[k][1], z = beats[k][2];
+    u64 kept;
+    if (N == 1) kept = ~(x | y | z);
+    else if (N == 2) kept = ~((x & y) | (x & z) | (y & z));
+    else kept = ~(x & y & z);
+    keep[k] = __builtin_amdgcn_inverse_ballot_w64(kept);
+  }
+}
+
 // ---- wave helpers -------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

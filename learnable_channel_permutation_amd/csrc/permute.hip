@@ -89,7 +89,8 @@ __device__ __forceinline__ void perm_prep(const float* __restrict__ P, const flo
 // at most a few blocks; the P fragments are (re)loaded into LDS when the
 // block changes. With `gfrag` the fragments come precomputed from global
 // memory (a coalesced copy), otherwise they are built here.
-template <int B, int MODE, int M>
+// NK: for M = 4, the N of N:M fixed at compile time (1..3), 0 = runtime N.
+template <int B, int MODE, int M, int NK>
 __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_kernel(
     const uint16_t* __restrict__ A, int rows, int cin, const float* __restrict__ colscale,
     const float* __restrict__ P, int transposeP, const u32x4* __restrict__ gfrag, int tpw,
@@ -202,25 +203,40 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
         for (int s = G::NSPLIT - 1; s >= 0; --s)
 #pragma unroll
           for (int p = 0; p < KS; ++p) sh = mfma32(FQ[(size_t)s * G::FRAG + (t * KS + p) * 64 + l], absw[p], sh);
-        float v[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = nan_to_ninf(sh[r]);
-        uint32_t keep = 0;
-#pragma unroll
-        for (int g = 0; g < 16 / M; ++g) keep |= nm_keep<M>(v + g * M, N) << (g * M);
-        const uint32_t other = (uint32_t)__shfl_xor((int)keep, 32, 64);
-        kw[t] = keep | (other << 16);
-
         floatx16 wh = {};
 #pragma unroll
         for (int p = 0; p < KS; ++p) wh = mfma32(F1[(t * KS + p) * 64 + l], cur[p], wh);
+        float v[16], a[16];
+        uint32_t keep = 0;
+        if constexpr (M == 4 && NK > 0) {
+          // the scores are sums of products of |W|, n_j and P (all >= +0), so
+          // nm_keep4_nonneg applies; each group's keep masks are used at once
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float a[8];
+          for (int r = 0; r < 16; ++r) v[r] = sh[r];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] = ((keep >> (8 * u + e)) & 1u) ? wh[8 * u + e] : 0.f;
-          aop[2 * t + u] = u32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7])};
+          for (int g = 0; g < 4; ++g) {
+            bool k4[4];
+            nm_keep4_nonneg<NK>(v + 4 * g, k4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              keep |= k4[q] ? (1u << (4 * g + q)) : 0u;
+              a[4 * g + q] = k4[q] ? wh[4 * g + q] : 0.f;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = nan_to_ninf(sh[r]);
+#pragma unroll
+          for (int g = 0; g < 16 / M; ++g) keep |= nm_keep<M>(v + g * M, N) << (g * M);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a[r] = ((keep >> r) & 1u) ? wh[r] : 0.f;
         }
+        const uint32_t other = (uint32_t)__shfl_xor((int)keep, 32, 64);
+        kw[t] = keep | (other << 16);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          aop[2 * t + u] = u32x4{pack2(a[8 * u], a[8 * u + 1]), pack2(a[8 * u + 2], a[8 * u + 3]),
+                                 pack2(a[8 * u + 4], a[8 * u + 5]), pack2(a[8 * u + 6], a[8 * u + 7])};
       }
       // mask words, block-major: the tile's 32 rows x TT words are contiguous
       if (h == 0 && i < rows) {
@@ -339,7 +355,7 @@ __global__ __launch_bounds__(256) void diff_kernel(const void* __restrict__ W, c
 // not depend on the split.
 static int perm_grid(int B, int mode) { return B == 128 ? 256 : (B == 64 && mode == PERM_FWD) ? 768 : 1024; }
 
-template <int B, int MODE, int M>
+template <int B, int MODE, int M, int NK = 0>
 static hipError_t perm_bf16_launch(const uint16_t* A, int rows, int cin, const float* colscale,
                                    const float* P, int transposeP, const u32x4* gfrag, void* out,
                                    int out_f32, uint32_t* bits, int N, hipStream_t s) {
@@ -348,7 +364,7 @@ static hipError_t perm_bf16_launch(const uint16_t* A, int rows, int cin, const f
   int grid = perm_grid(B, MODE);
   const int tpw = (total + grid - 1) / grid;
   grid = (total + tpw - 1) / tpw;
-  permute_bf16_kernel<B, MODE, M><<<grid, G::THREADS, G::LDS, s>>>(A, rows, cin, colscale, P, transposeP,
+  permute_bf16_kernel<B, MODE, M, NK><<<grid, G::THREADS, G::LDS, s>>>(A, rows, cin, colscale, P, transposeP,
                                                                     gfrag, tpw, out, out_f32, bits, N);
   return hipGetLastError();
 }
@@ -358,6 +374,11 @@ static hipError_t perm_bf16_m(const uint16_t* A, int rows, int cin, const float*
                               int transposeP, const u32x4* gfrag, void* out, int out_f32, uint32_t* bits,
                               int N, int M, hipStream_t s) {
   if (M == 8) return perm_bf16_launch<B, MODE, 8>(A, rows, cin, colscale, P, transposeP, gfrag, out, out_f32, bits, N, s);
+  switch (N) {
+    case 1: return perm_bf16_launch<B, MODE, 4, 1>(A, rows, cin, colscale, P, transposeP, gfrag, out, out_f32, bits, N, s);
+    case 2: return perm_bf16_launch<B, MODE, 4, 2>(A, rows, cin, colscale, P, transposeP, gfrag, out, out_f32, bits, N, s);
+    case 3: return perm_bf16_launch<B, MODE, 4, 3>(A, rows, cin, colscale, P, transposeP, gfrag, out, out_f32, bits, N, s);
+  }
   return perm_bf16_launch<B, MODE, 4>(A, rows, cin, colscale, P, transposeP, gfrag, out, out_f32, bits, N, s);
 }
 
