@@ -318,3 +318,16 @@ def test_step_full_size_bench_layer():
     say("step full size", spec.name)
     got = _run_step(lay, spec)
     _check_step(lay, spec, got)
+
+
+@pytest.mark.parametrize("ci", [1, 3, 4])
+def test_step_full_size_other_layers(ci):
+    """The other seeded layers at their full sizes, through the same session
+    path the benchmark uses: 4096 x 4096 (forward only), 13824 x 5120 (B = 128,
+    4:8) and 28672 x 8192, each against the full float64 oracle."""
+    spec = lcp_synth.CONFIGS[ci]
+    lay = lcp_synth.make_layer(spec)
+    say("step full size", spec.name)
+    got = _run_step(lay, spec, backward=spec.backward)
+    _check_step(lay, spec, got, backward=spec.backward)
+
