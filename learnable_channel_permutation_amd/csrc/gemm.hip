@@ -6,9 +6,9 @@
 // bf16 kernel (gfx950): BM x BN x 64 tiles, 8 waves (two per SIMD) in a
 // 4 x 2 layout, each wave owning (BM/4) x (BN/2) of the tile as MFMA 32x32x16
 // blocks with fp32 accumulators. Operand tiles move global -> LDS with
-// 16-byte direct-to-LDS loads (no register staging) into a two-stage ring;
-// one barrier per K step, and the next tile's loads are in flight while the
-// current one is multiplied. Chunk c of row r is stored at position
+// 16-byte direct-to-LDS loads (no register staging) into a two- or
+// three-stage ring; one barrier per K step, and the next tiles' loads are in
+// flight while the current one is multiplied. Chunk c of row r is stored at position
 // c ^ ((r >> 1) & 7): the 16-byte fragment reads of 16 consecutive rows then
 // cover all 64 LDS banks. Inside a K step the MFMAs of one 16-wide sub-step
 // are interleaved one-to-one with the fragment reads of the next
@@ -74,10 +74,16 @@ __device__ __forceinline__ void pin_schedule() {
   }
 }
 
-template <int BM, int BN>
-constexpr size_t gemm_lds_bytes() { return (size_t)2 * (BM + BN) * GBK * 2; }
+template <int BM, int BN, int S>
+constexpr size_t gemm_lds_bytes() { return (size_t)S * (BM + BN) * GBK * 2; }
 
-template <int BM, int BN, int EPI>
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited on)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int EPI, int S>
 __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M,
     int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, float* __restrict__ part,
@@ -151,16 +157,23 @@ __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
     pin_schedule<FM, FN>();
   };
 
+  // S-stage ring: tiles kt + 1 .. kt + S - 2 stay in flight while tile kt is
+  // multiplied. At step kt this thread waits until only the loads issued for
+  // later tiles are outstanding (its part of tile kt has landed); the barrier
+  // then makes every thread's part visible and guarantees that the stage of
+  // tile kt - 1 is no longer read before it is refilled with tile kt + S - 1.
   const int nk = (K + GBK - 1) / GBK;
-  issue(0, 0);
+  constexpr int NL = AI + BI;                              // load instructions per tile
+  static_assert(S == 2 || S == 3, "two or three stages");
+#pragma unroll
+  for (int q = 0; q < S - 1; ++q)
+    if (q < nk) issue(q, q * GBK);
   for (int kt = 0; kt < nk; ++kt) {
-    // this thread's loads of tile kt have landed (nothing later is in flight
-    // yet); the barrier makes every thread's part visible and also guarantees
-    // the other stage is no longer being read before it is refilled
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    if (S == 3 && kt + 1 < nk) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * GBK);
-    compute(kt & 1);
+    if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * GBK);
+    compute(kt % S);
   }
 
   // ---- epilogue: lane (h, ln) of block (i, j) holds row m0 + wm*WM + 32i + ln,
@@ -283,9 +296,10 @@ __global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restr
 }
 
 // ---- launchers -------------------------------------------------------------------
-// error GEMM: 256 x 128 tiles (the 4096 x 2048 residual is exactly 256 tiles);
-// dD GEMM: 256 x 256 tiles.
-constexpr int EBM = 256, EBN = 128, DBM = 256, DBN = 256;
+// error GEMM: 256 x 128 tiles (the 4096 x 2048 residual is exactly 256 tiles)
+// with a three-stage ring (144 KB of LDS; its long K loop streams more
+// operand bytes per flop); dD GEMM: 256 x 256 tiles, two stages (128 KB).
+constexpr int EBM = 256, EBN = 128, ES = 3, DBM = 256, DBN = 256, DS = 2;
 
 int gemm_error_parts(int M, int N, int bf16) {
   if (bf16) return ((M + EBM - 1) / EBM) * ((N + EBN - 1) / EBN);
@@ -296,7 +310,7 @@ hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm
                                   int N_valid, int N_store, int K, uint16_t* C, int ldc,
                                   float* part, hipStream_t s) {
   const int G = gemm_error_parts(M, N_store, 1);
-  gemm_bf16_kernel<EBM, EBN, EPI_ERR><<<G, GNT, gemm_lds_bytes<EBM, EBN>(), s>>>(
+  gemm_bf16_kernel<EBM, EBN, EPI_ERR, ES><<<G, GNT, gemm_lds_bytes<EBM, EBN, ES>(), s>>>(
       A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr);
   return hipGetLastError();
 }
@@ -304,7 +318,7 @@ hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm
 hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
                                int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s) {
   const int G = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
-  gemm_bf16_kernel<DBM, DBN, EPI_DD><<<G, GNT, gemm_lds_bytes<DBM, DBN>(), s>>>(
+  gemm_bf16_kernel<DBM, DBN, EPI_DD, DS><<<G, GNT, gemm_lds_bytes<DBM, DBN, DS>(), s>>>(
       A, lda, Bm, ldb, M, N, N, K, C, ldc, nullptr, E);
   return hipGetLastError();
 }
