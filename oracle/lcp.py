@@ -20,6 +20,10 @@ design notes):
   definition asks for the permuted, pruned weight closest to the dense one on
   the layer's outputs; this is that distance.
 * The mask is held constant in the backward pass (no straight-through term).
+* Hardening (Method 2) is optional: the forward may replace P_hat by the
+  permutation maximising Tr(P^T P_hat) per block; the backward then takes the
+  block adjoint at the hard P and passes it unchanged to the adjoint of the
+  soft Sinkhorn (straight-through estimator).
 * Ties inside an N:M group go to the lower permuted position; NaN scores rank
   as -inf; -0 ties with +0. The keep decision is taken on float32 scores, the
   precision the GPU kernel decides in.
@@ -182,12 +186,15 @@ def pruning_error(D, X):
 
 
 # forward step ---------------------------------------------------------------
-def step_forward(W, X, logits, tau, iters, N, M, P=None, mask=None):
+def step_forward(W, X, logits, tau, iters, N, M, P=None, mask=None, hard=False):
     """One LCP forward step (O1 .. O7). Returns a dict of every intermediate.
 
     P overrides the Sinkhorn output (used to feed hard permutations); mask
     overrides the N:M selection (used to freeze the mask for finite
-    differences)."""
+    differences). hard=True replaces the soft P_hat by its hardened
+    permutation before the block permutation (PermLLM summary, Method 2); the
+    dict then holds the hard matrix as "P" and the Sinkhorn output as
+    "P_soft"."""
     W = _f64(W)
     X = _f64(X)
     n = colnorm(X)
@@ -196,15 +203,18 @@ def step_forward(W, X, logits, tau, iters, N, M, P=None, mask=None):
     if P is None:
         P, tr = sinkhorn(logits, tau, iters, trace=True)
     P = _f64(P)
+    P_soft = P
+    if hard:
+        P = harden(P_soft)
     W_hat = block_permute(W, P)
     S_hat = block_permute(S, P)
     if mask is None:
         mask = nm_mask(S_hat, N, M)
     A, W_tilde, D = unpermute_diff(W, W_hat, mask, P)
     R, E = pruning_error(D, X)
-    return {"n": n, "S": S, "P": P, "trace": tr, "W_hat": W_hat, "S_hat": S_hat,
-            "mask": mask, "A": A, "W_tilde": W_tilde, "D": D, "R": R, "E": E,
-            "tau": float(tau), "iters": int(iters)}
+    return {"n": n, "S": S, "P": P, "P_soft": P_soft, "hard": bool(hard), "trace": tr,
+            "W_hat": W_hat, "S_hat": S_hat, "mask": mask, "A": A, "W_tilde": W_tilde,
+            "D": D, "R": R, "E": E, "tau": float(tau), "iters": int(iters)}
 
 
 # O8 .. O10 ------------------------------------------------------------------
@@ -248,7 +258,10 @@ def step_backward(fw, X, W):
 
     dR = R / E (zero when E = 0); G = dE/dW_tilde = -dR X; then the block
     adjoint and the Sinkhorn adjoint. Requires a forward dict whose P came
-    from the Sinkhorn (trace present)."""
+    from the Sinkhorn (trace present). For a hardened forward the block
+    adjoint is taken at the hard P and its result is handed unchanged to the
+    Sinkhorn adjoint of the soft P_hat (straight-through estimator, PermLLM
+    summary, Method 2)."""
     if fw["trace"] is None:
         raise ValueError("forward step must come from logits")
     E = fw["E"]
@@ -256,7 +269,7 @@ def step_backward(fw, X, W):
     dR = R / E if E > 0 else np.zeros_like(R)
     G = -(dR @ _f64(X))
     dP = block_adjoint(G, fw["A"], W, fw["P"], fw["mask"])
-    dL = sinkhorn_adjoint(dP, fw["P"], fw["trace"], fw["tau"])
+    dL = sinkhorn_adjoint(dP, fw["P_soft"], fw["trace"], fw["tau"])
     return {"dR": dR, "G": G, "dP": dP, "dlogits": dL}
 
 

@@ -470,6 +470,74 @@ def pin_colnorm(o):
     assert np.allclose(o.colnorm(X), want, rtol=1e-14, atol=0)
 
 
+def pin_harden_bruteforce(o):
+    """Hardening (PermLLM summary, Method 2: the permutation matrix P that
+    maximises Tr(P^T P_hat)) against brute force over all B! permutations."""
+    rng = _rng(23)
+    for B in (3, 4, 5, 6):
+        for trial in range(3):
+            Ph = rng.random((1, B, B))
+            best, arg = -math.inf, None
+            for perm in itertools.permutations(range(B)):
+                val = sum(Ph[0, j, perm[j]] for j in range(B))     # row j -> column perm[j]
+                if val > best:
+                    best, arg = val, perm
+            want = np.zeros((B, B))
+            want[np.arange(B), list(arg)] = 1.0
+            assert np.array_equal(o.harden(Ph)[0], want), (B, trial)
+
+
+def pin_hard_forward_planted(o):
+    """Logits peaked around a planted block permutation: the hardened forward
+    is exactly the forward of the planted hard P (same P, mask and E), while
+    the soft Sinkhorn output is still visibly soft."""
+    rng = _rng(24)
+    cout, cin, T, B = 6, 16, 9, 8
+    W = rng.standard_normal((cout, cin))
+    X = rng.standard_normal((T, cin))
+    nb = cin // B
+    Pi = np.zeros((nb, B, B))
+    for b in range(nb):
+        Pi[b, np.arange(B), rng.permutation(B)] = 1.0
+    lg = 2.0 * Pi + 0.05 * rng.standard_normal((nb, B, B))
+    fh = o.step_forward(W, X, lg, 1.0, 3, 2, 4, hard=True)
+    fp = o.step_forward(W, X, None, 1.0, 3, 2, 4, P=Pi)
+    assert np.array_equal(fh["P"], Pi)
+    assert np.max(np.abs(fh["P_soft"] - Pi)) > 0.1
+    assert np.array_equal(fh["mask"], fp["mask"])
+    assert abs(fh["E"] - fp["E"]) <= 1e-12 * fp["E"]
+
+
+def pin_straight_through_gradient_fd(o):
+    """Hardened step: the gradient is the straight-through estimate
+    dE/dLambda = J^T g, with g = dE/dP at the hard P (mask frozen) and J the
+    Jacobian of the soft Sinkhorn output. Both g and J^T g are taken by
+    central differences here, independently of the adjoint formulas."""
+    rng = _rng(25)
+    cout, cin, T, B, tau, L = 5, 8, 7, 4, 0.8, 3
+    W = rng.standard_normal((cout, cin))
+    X = rng.standard_normal((T, cin))
+    lg = rng.standard_normal((cin // B, B, B))
+    fw = o.step_forward(W, X, lg, tau, L, 2, 4, hard=True)
+    got = o.step_backward(fw, X, W)["dlogits"]
+    Ph, mask = fw["P"], fw["mask"]
+    h = 1e-6
+    gP = np.zeros_like(Ph)
+    for idx in np.ndindex(Ph.shape):
+        pp = Ph.copy(); pp[idx] += h
+        pm = Ph.copy(); pm[idx] -= h
+        ep = o.step_forward(W, X, None, tau, L, 2, 4, P=pp, mask=mask)["E"]
+        em = o.step_forward(W, X, None, tau, L, 2, 4, P=pm, mask=mask)["E"]
+        gP[idx] = (ep - em) / (2 * h)
+    fd = np.zeros_like(lg)
+    for idx in np.ndindex(lg.shape):
+        lp = lg.copy(); lp[idx] += h
+        lm = lg.copy(); lm[idx] -= h
+        fd[idx] = (np.sum(gP * o.sinkhorn(lp, tau, L)) - np.sum(gP * o.sinkhorn(lm, tau, L))) / (2 * h)
+    err = np.linalg.norm(got - fd) / np.linalg.norm(fd)
+    assert err < 1e-6, err
+
+
 ALL_PINS = [
     pin_sinkhorn_2x2_golden, pin_sinkhorn_uniform, pin_sinkhorn_closed_form,
     pin_sinkhorn_closed_form_values, pin_sinkhorn_doubly_stochastic,
@@ -479,5 +547,6 @@ ALL_PINS = [
     pin_nm_mask_bruteforce, pin_nm_mask_counts, pin_pack_bits,
     pin_identity_is_wanda, pin_hard_perm_error, pin_gram_identity,
     pin_cin8_enumeration, pin_step_gradient_fd, pin_block_adjoint_fd,
-    pin_zero_error_gradient, pin_colnorm,
+    pin_zero_error_gradient, pin_colnorm, pin_harden_bruteforce,
+    pin_hard_forward_planted, pin_straight_through_gradient_fd,
 ]

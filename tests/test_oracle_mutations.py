@@ -148,6 +148,26 @@ def _backward_unscaled(fw, X, W):
     return _orig["step_backward"](fw2, X, W)
 
 
+def _harden_minimise(P):
+    return _orig["harden"](-np.asarray(P, dtype=np.float64))
+
+
+def _harden_transposed(P):
+    return np.transpose(_orig["harden"](P), (0, 2, 1))
+
+
+def _ste_hard_in_sinkhorn_adjoint(fw, X, W):
+    fw2 = dict(fw)
+    fw2["P_soft"] = fw["P"]
+    return _orig["step_backward"](fw2, X, W)
+
+
+def _ste_soft_in_block_adjoint(fw, X, W):
+    fw2 = dict(fw)
+    fw2["P"] = fw["P_soft"]
+    return _orig["step_backward"](fw2, X, W)
+
+
 MUTATIONS = [
     ("sinkhorn", _sinkhorn_cols_first),
     ("sinkhorn", _sinkhorn_times_tau),
@@ -173,6 +193,10 @@ MUTATIONS = [
     ("sinkhorn_adjoint", _adjoint_no_tau),
     ("sinkhorn_adjoint", _adjoint_forward_order),
     ("step_backward", _backward_unscaled),
+    ("harden", _harden_minimise),
+    ("harden", _harden_transposed),
+    ("step_backward", _ste_hard_in_sinkhorn_adjoint),
+    ("step_backward", _ste_soft_in_block_adjoint),
 ]
 
 # the full 8! enumeration is covered by the plain pin run; the rest are fast
