@@ -76,13 +76,17 @@ typedef struct lcp_cfg {
   int   iters;  /* Sinkhorn iterations L >= 1 (one = row step then column step) */
   float tau;    /* temperature > 0                                              */
   int   N, M;   /* keep N of every M; M in {4, 8}, 1 <= N < M, B % M == 0       */
+  int   harden; /* 0: the step uses the soft P_hat. 1: the forward uses the
+                   hardened P of lcp_harden ([PermLLM] Method 2) and the
+                   backward is straight-through: dE/dP at the hard P is handed
+                   unchanged to the adjoint of the soft Sinkhorn.              */
 } lcp_cfg;
 
 /* Optional per-kernel timing hooks: hipEvent_t handles (as void*) recorded on
  * the step's stream immediately before (start[i]) and after (stop[i]) kernel i
  * of the step. NULL entries are skipped; a NULL lcp_timing* records nothing.
  * Forward kernels: 0 Sinkhorn, 1 permute+mask+unpermute, 2 error GEMM,
- * 3 error finalisation. Backward kernels: 0 dD GEMM, 1 block adjoint, 2 Sinkhorn adjoint. */
+ * 3 error finalisation, 4 hardening (harden = 1 only). Backward kernels: 0 dD GEMM, 1 block adjoint, 2 Sinkhorn adjoint. */
 typedef struct lcp_timing {
   void* start[8];
   void* stop[8];
@@ -111,6 +115,19 @@ int lcp_sinkhorn(const float* logits, float* P, int nb, int B, int iters,
  * from [PermLLM] Method 1 by the chain rule. dlogits must not alias dP. */
 int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B,
                      int iters, float tau, float* dlogits, void* stream);
+
+/* lcp_harden - per block, the permutation matrix P maximising Tr(P^T P_hat)
+ * ([PermLLM] Method 2: the hard permutation used in the forward pass), i.e.
+ * the maximum-weight assignment of source channels j (rows) to permuted
+ * positions k (columns). Exact (shortest augmenting paths in double
+ * precision); among equally good assignments the result is deterministic.
+ *   P: [nb][B][B] fp32 in (finite entries);
+ *   P_hard (nullable): [nb][B][B] fp32 out, 1 where assigned, else 0;
+ *   perm (nullable): [nb][B] int32 out, perm[b][k] = the row j assigned to
+ *   column k. At least one output; P_hard must not alias P. B in {32,64,128}.
+ */
+int lcp_harden(const float* P, int nb, int B, float* P_hard, int32_t* perm,
+               void* stream);
 
 /* ---------------------------------------------------------------------------
  * lcp_colnorm - norms[j] = ||X[:, j]||_2 over the T tokens, fp32 accumulation.
@@ -184,9 +201,11 @@ int lcp_error(const void* W, const void* Wt, const void* X, lcp_dtype dt,
 int lcp_step_workspace_bytes(int cout, int cin, int T, int B, int iters,
                              lcp_dtype dt, size_t* bytes);
 
-/* lcp_step_fwd - Sinkhorn, permute, importance, N:M mask, un-permute,
- * difference, error GEMM: *err = E. Optional copies: P_out [nb][B][B] fp32,
- * bits_out [cout][cin/32] uint32 (the mask in permuted positions). */
+/* lcp_step_fwd - Sinkhorn, (hardening,) permute, importance, N:M mask,
+ * un-permute, difference, error GEMM: *err = E. Optional copies: P_out
+ * [nb][B][B] fp32 (the P the forward used: P_hat, or the hard P when
+ * c->harden), bits_out [cout][cin/32] uint32 (the mask in permuted
+ * positions). */
 int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c,
                  void* ws, size_t ws_bytes, float* err, float* P_out,
                  uint32_t* bits_out, const lcp_timing* tm, void* stream);

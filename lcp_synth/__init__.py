@@ -165,6 +165,18 @@ def random_logits(seed: int, nb: int, B: int, scale: float = 1.0) -> np.ndarray:
     return (scale * rng.standard_normal((nb, B, B))).astype(np.float32)
 
 
+def planted_logits(seed: int, nb: int, B: int, peak: float = 3.0, noise_std: float = 0.1):
+    """Per block peak*Pi_b + N(0, noise_std^2) with a random permutation matrix
+    Pi_b (Pi_b[j, pi_b(j)] = 1); returns (float32 logits [nb, B, B], Pi as
+    float64 [nb, B, B])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Pi = np.zeros((nb, B, B))
+    for b in range(nb):
+        Pi[b, np.arange(B), rng.permutation(B)] = 1.0
+    lg = peak * Pi + rng.normal(0.0, noise_std, size=(nb, B, B))
+    return lg.astype(np.float32), Pi
+
+
 def random_matrix(seed: int, shape, std: float = 1.0, dtype: str = "f32") -> np.ndarray:
     """Seeded N(0, std^2) matrix as float32 values (bf16-representable for bf16)."""
     rng = np.random.Generator(np.random.PCG64(seed))

@@ -11,7 +11,7 @@ import torch
 
 from . import _lib
 from ._lib import (LCP_BF16, LCP_F32, LcpError, lcp_colnorm, lcp_error,  # noqa: F401
-                   lcp_error_workspace_bytes, lcp_layer_init, lcp_nm_mask, lcp_permute,
+                   lcp_error_workspace_bytes, lcp_harden, lcp_layer_init, lcp_nm_mask, lcp_permute,
                    lcp_sinkhorn, lcp_sinkhorn_bwd, lcp_step_bwd, lcp_step_fwd,
                    lcp_step_workspace_bytes, lcp_xt_pitch, make_cfg, make_layer, make_timing)
 
@@ -23,10 +23,11 @@ class LayerSession:
 
     Holds W and X (caller tensors on one GPU), the per-layer setup written by
     lcp_layer_init (column norms; X transposed for bf16 layers) and one step
-    workspace sized by lcp_step_workspace_bytes.
+    workspace sized by lcp_step_workspace_bytes. harden=True runs the
+    hardened forward with the straight-through backward.
     """
 
-    def __init__(self, W, X, B, iters, tau, N, M, stream=None):
+    def __init__(self, W, X, B, iters, tau, N, M, stream=None, harden=False):
         if W.device != X.device or W.dtype != X.dtype:
             raise ValueError("W and X must share device and dtype")
         self.W, self.X = W, X
@@ -42,7 +43,7 @@ class LayerSession:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.err = torch.empty(1, dtype=torch.float32, device=dev)
         self.layer = make_layer(W, X, self.norms, B, self.Xt)
-        self.cfg = make_cfg(iters, tau, N, M)
+        self.cfg = make_cfg(iters, tau, N, M, harden)
         self.init(stream)
 
     def init(self, stream=None):

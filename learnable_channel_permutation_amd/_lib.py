@@ -28,7 +28,7 @@ EXPORTS = [
     "lcp_status_string", "lcp_version", "lcp_sinkhorn", "lcp_sinkhorn_bwd", "lcp_colnorm",
     "lcp_xt_pitch", "lcp_layer_init", "lcp_permute", "lcp_nm_mask",
     "lcp_error_workspace_bytes", "lcp_error", "lcp_step_workspace_bytes", "lcp_step_fwd",
-    "lcp_step_bwd",
+    "lcp_step_bwd", "lcp_harden",
 ]
 
 
@@ -40,7 +40,7 @@ class lcp_layer(ctypes.Structure):
 
 class lcp_cfg(ctypes.Structure):
     _fields_ = [("iters", ctypes.c_int), ("tau", ctypes.c_float), ("N", ctypes.c_int),
-                ("M", ctypes.c_int)]
+                ("M", ctypes.c_int), ("harden", ctypes.c_int)]
 
 
 class lcp_timing(ctypes.Structure):
@@ -65,6 +65,7 @@ def _load():
         "lcp_version": (i, []),
         "lcp_sinkhorn": (i, [vp, vp, i, i, i, f, vp]),
         "lcp_sinkhorn_bwd": (i, [vp, vp, i, i, i, f, vp, vp]),
+        "lcp_harden": (i, [vp, i, i, vp, vp, vp]),
         "lcp_colnorm": (i, [vp, i, i, i, vp, vp]),
         "lcp_xt_pitch": (i, [i]),
         "lcp_layer_init": (i, [vp, i, i, i, vp, vp, vp]),
@@ -128,6 +129,11 @@ def lcp_sinkhorn_bwd(logits, dP, iters, tau, dlogits, stream=None):
                                                            _p(dlogits), _stream(stream)))
 
 
+def lcp_harden(P, P_hard=None, perm=None, stream=None):
+    nb, B, _ = P.shape
+    return _check("lcp_harden", LIB.lcp_harden(_p(P), nb, B, _p(P_hard), _p(perm), _stream(stream)))
+
+
 def lcp_colnorm(X, norms, stream=None):
     T, cin = X.shape
     return _check("lcp_colnorm", LIB.lcp_colnorm(_p(X), dtype_code(X), T, cin, _p(norms), _stream(stream)))
@@ -182,8 +188,8 @@ def make_layer(W, X, norms, B, Xt=None):
                      dtype_code(W), cout, cin, X.shape[0], B)
 
 
-def make_cfg(iters, tau, N, M):
-    return lcp_cfg(int(iters), float(tau), int(N), int(M))
+def make_cfg(iters, tau, N, M, harden=False):
+    return lcp_cfg(int(iters), float(tau), int(N), int(M), 1 if harden else 0)
 
 
 def make_timing(starts=(), stops=()):

@@ -25,7 +25,7 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int pitch_of(int T) { return (T + 63) / 64 * 64; }
 
 struct StepLayout {
-  size_t P, off, bits, D, R, part, E, adj, fragF, fragA, total;
+  size_t P, Ph, off, bits, D, R, part, E, adj, fragF, fragA, total;
   int nb, pitch, nparts;
   AdjSplit sp;
 };
@@ -39,6 +39,7 @@ StepLayout step_layout(int cout, int cin, int T, int B, int iters, lcp_dtype dt)
   const bool bf = dt == LCP_BF16;
   size_t o = 0;
   L.P = o;     o += align_up((size_t)L.nb * B * B * 4);
+  L.Ph = o;    o += align_up((size_t)L.nb * B * B * 4);
   L.off = o;   o += align_up((size_t)L.nb * iters * 2 * B * 4);
   L.bits = o;  o += align_up((size_t)cout * (cin / 32) * 4);
   L.D = o;     o += align_up((size_t)cout * cin * esize(dt));
@@ -59,6 +60,7 @@ int check_step_args(const lcp_layer* L, const float* logits, const lcp_cfg* c) {
   if (L->cout <= 0 || L->cin <= 0 || L->T <= 0 || L->B <= 0) return LCP_E_INVAL;
   if (c->iters < 1 || !good_tau(c->tau)) return LCP_E_INVAL;
   if (c->M <= 0 || c->N < 1 || c->N >= c->M) return LCP_E_INVAL;
+  if (c->harden != 0 && c->harden != 1) return LCP_E_INVAL;
   if (L->cin % L->B != 0 || L->B % c->M != 0) return LCP_E_INVAL;
   if (!good_B(L->B)) return LCP_E_UNSUPPORTED;
   if (c->M != 4 && c->M != 8) return LCP_E_UNSUPPORTED;
@@ -125,6 +127,15 @@ int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B, int it
   if (!fits_i32(nb, (long long)B * B) || !aligned16(logits) || !aligned16(dP) || !aligned16(dlogits))
     return LCP_E_INVAL;
   LCP_RUN(launch_sinkhorn_bwd(logits, dP, nullptr, nullptr, dlogits, nb, B, iters, tau, S(stream)));
+  return LCP_OK;
+}
+
+int lcp_harden(const float* P, int nb, int B, float* P_hard, int32_t* perm, void* stream) {
+  if (!P || nb <= 0 || B <= 0 || (!P_hard && !perm)) return LCP_E_INVAL;
+  if (!good_B(B)) return LCP_E_UNSUPPORTED;
+  if (!fits_i32(nb, (long long)B * B)) return LCP_E_INVAL;
+  if (P_hard == P) return LCP_E_INVAL;
+  LCP_RUN(launch_harden(P, nb, B, P_hard, perm, nullptr, nullptr, nullptr, S(stream)));
   return LCP_OK;
 }
 
@@ -257,16 +268,26 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
 
   u32x4* fragF = (u32x4*)(base + Ly.fragF);
   u32x4* fragA = (u32x4*)(base + Ly.fragA);
+  const bool hard = c->harden != 0;
   tmr.start(0);
-  LCP_RUN(launch_sinkhorn_fwd(logits, P, off, Ly.nb, L->B, c->iters, c->tau, L->norms, bf ? fragF : nullptr,
-                              bf ? fragA : nullptr, s));
+  LCP_RUN(launch_sinkhorn_fwd(logits, P, off, Ly.nb, L->B, c->iters, c->tau, L->norms,
+                              (bf && !hard) ? fragF : nullptr, (bf && !hard) ? fragA : nullptr, s));
   tmr.stop(0);
+  // hardened forward: the block permutation, mask and un-permute use the
+  // per-block assignment of P_hat ([PermLLM] Method 2)
+  float* Pu = P;
+  if (hard) {
+    Pu = (float*)(base + Ly.Ph);
+    tmr.start(4);
+    LCP_RUN(launch_harden(P, Ly.nb, L->B, Pu, nullptr, L->norms, bf ? fragF : nullptr, bf ? fragA : nullptr, s));
+    tmr.stop(4);
+  }
   tmr.start(1);
   if (bf)
-    LCP_RUN(launch_permute_bf16((const uint16_t*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, fragF, PERM_FWD,
+    LCP_RUN(launch_permute_bf16((const uint16_t*)L->W, L->cout, L->cin, L->norms, Pu, L->B, 0, fragF, PERM_FWD,
                                 D, 0, bits, c->N, c->M, s));
   else
-    LCP_RUN(launch_permute_f32((const float*)L->W, L->cout, L->cin, L->norms, P, L->B, 0, PERM_FWD, (float*)D,
+    LCP_RUN(launch_permute_f32((const float*)L->W, L->cout, L->cin, L->norms, Pu, L->B, 0, PERM_FWD, (float*)D,
                                bits, c->N, c->M, s));
   tmr.stop(1);
   tmr.start(2);
@@ -281,7 +302,7 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
   LCP_RUN(launch_error_finalize(part, Ly.nparts, Ews, err, s));
   tmr.stop(3);
   if (P_out)
-    LCP_RUN(hipMemcpyAsync(P_out, P, (size_t)Ly.nb * L->B * L->B * 4, hipMemcpyDeviceToDevice, s));
+    LCP_RUN(hipMemcpyAsync(P_out, Pu, (size_t)Ly.nb * L->B * L->B * 4, hipMemcpyDeviceToDevice, s));
   if (bits_out) LCP_RUN(launch_bits_rowmajor(bits, L->cout, L->cin, L->B, bits_out, s));
   return LCP_OK;
 }
@@ -298,7 +319,9 @@ int lcp_step_bwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
   if (rc != LCP_OK) return rc;
 
   char* base = (char*)ws;
-  const float* P = (const float*)(base + Ly.P);
+  // the block adjoint is taken at the P the forward used (the hard P when
+  // hardened: straight-through, the Sinkhorn adjoint below stays soft)
+  const float* P = (const float*)(base + (c->harden ? Ly.Ph : Ly.P));
   const float* off = (const float*)(base + Ly.off);
   const uint32_t* bits = (const uint32_t*)(base + Ly.bits);
   void* Gd = base + Ly.D;           // G reuses the forward's D buffer

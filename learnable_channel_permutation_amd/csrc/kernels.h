@@ -29,6 +29,12 @@ hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, const AdjSp
                                const float* off, float* dlogits, int nb, int B, int iters,
                                float tau, hipStream_t s);
 
+// Hardening (harden.hip): per block the permutation maximising Tr(P^T P_hat).
+// Any of P_hard ([nb][B][B] 0/1 fp32), perm ([nb][B]: source row of each
+// position) and the fragment sets (with the norms n) may be null.
+hipError_t launch_harden(const float* P, int nb, int B, float* P_hard, int* perm, const float* n, u32x4* fwd,
+                         u32x4* adj, hipStream_t s);
+
 // Per-layer setup (layer.hip): column norms, optional bf16 transpose.
 hipError_t launch_colnorm_f32(const float* X, int T, int cin, float* norms, hipStream_t s);
 hipError_t launch_layer_init_bf16(const uint16_t* X, int T, int cin, int pitch, float* norms,

@@ -331,3 +331,83 @@ def test_step_full_size_other_layers(ci):
     got = _run_step(lay, spec, backward=spec.backward)
     _check_step(lay, spec, got, backward=spec.backward)
 
+
+# -------------------------------------------------------------- hardening --
+def _assignment_value(P, perm):
+    nb, B, _ = P.shape
+    return np.array([P[b, perm[b], np.arange(B)].sum() for b in range(nb)])
+
+
+@pytest.mark.parametrize("B", [32, 64, 128])
+@pytest.mark.parametrize("kind", ["sinkhorn", "planted", "ties"])
+def test_harden_assignment(B, kind):
+    """lcp_harden against the oracle's assignment of the same fp32 P_hat:
+    identical permutations where the optimum is unique, and an optimal,
+    valid permutation when every assignment ties."""
+    nb = 9
+    if kind == "sinkhorn":
+        P = oracle.sinkhorn(lcp_synth.random_logits(300 + B, nb, B).astype(np.float64), 1.0, 5).astype(np.float32)
+    elif kind == "planted":
+        lg, _ = lcp_synth.planted_logits(400 + B, nb, B)
+        P = oracle.sinkhorn(lg.astype(np.float64), 1.0, 5).astype(np.float32)
+    else:
+        P = np.full((nb, B, B), 1.0 / B, dtype=np.float32)
+    say("harden", B, kind)
+    d_P = up(P)
+    d_hard = torch.full((nb, B, B), 5.0, dtype=torch.float32, device=DEV)
+    d_perm = torch.full((nb, B), -7, dtype=torch.int32, device=DEV)
+    L.lcp_harden(d_P, d_hard, d_perm)
+    torch.cuda.synchronize()
+    perm = d_perm.cpu().numpy()
+    hard = down(d_hard)
+    for b in range(nb):
+        assert sorted(perm[b].tolist()) == list(range(B))
+    want_hard = np.zeros((nb, B, B), dtype=np.float32)
+    for b in range(nb):
+        want_hard[b, perm[b], np.arange(B)] = 1.0
+    assert np.array_equal(hard, want_hard)
+    ref = oracle.harden(P.astype(np.float64))
+    ref_perm = np.argmax(ref, axis=1)                  # row assigned to each column
+    P64 = P.astype(np.float64)
+    if kind == "ties":
+        assert np.allclose(_assignment_value(P64, perm), _assignment_value(P64, ref_perm), rtol=0, atol=1e-12)
+    else:
+        assert np.array_equal(perm, ref_perm)
+
+
+SMALL_HARD = [
+    # (config index, cout, cin, T)
+    (0, 256, 256, 256),
+    (1, 300, 512, 200),
+    (2, 270, 640, 130),
+    (3, 257, 512, 96),
+]
+
+
+@pytest.mark.parametrize("ci,cout,cin,T", SMALL_HARD)
+def test_step_hardened(ci, cout, cin, T):
+    """Hardened forward (Method 2) and straight-through backward against the
+    oracle: the hard P exactly, the mask, E and the gradient."""
+    spec = lcp_synth.CONFIGS[ci]
+    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
+    lg, Pi = lcp_synth.planted_logits(500 + ci, cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
+    say("step hardened", spec.name, cout, cin, T)
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    s = lcp.LayerSession(up(lay.W, tdt), up(lay.X, tdt), spec.B, spec.iters, spec.tau, spec.N, spec.M,
+                         harden=True)
+    d_lg = up(lg)
+    P = torch.empty_like(d_lg)
+    bits = empty_bits(lay.cout, lay.cin)
+    err = s.forward(d_lg, P_out=P, bits_out=bits)
+    dl = s.backward(d_lg)
+    torch.cuda.synchronize()
+    fw = oracle.step_forward(lay.W, lay.X, lg, spec.tau, spec.iters, spec.N, spec.M, hard=True)
+    assert np.array_equal(down(P), fw["P"])
+    assert np.max(np.abs(fw["P_soft"] - fw["P"])) > 0.05          # the soft P_hat is not hard
+    agree = bit_agreement(bits_down(bits), oracle.pack_bits(fw["mask"]), lay.cout * lay.cin)
+    assert agree >= 0.999, agree
+    assert abs(float(err.item()) - fw["E"]) / fw["E"] < 1e-2
+    bw = oracle.step_backward(fw, lay.X, lay.W)
+    r = rel_fro(down(dl), bw["dlogits"])
+    assert r < 2e-2, r
+
