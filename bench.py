@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=None, help="layer config index (default: the bench layer)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--harden", action="store_true",
+                    help="hardened forward + straight-through backward (another workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (HBM counter calibration)")
@@ -115,7 +117,7 @@ class _Ev:
         self.cuda_event = h.value
 
 
-def cpu_baseline(spec, lay):
+def cpu_baseline(spec, lay, hard=False):
     """The float64 oracle, untuned, for one full forward + backward step of the
     same layer on the host cores (one step is the sample)."""
     import oracle
@@ -125,12 +127,13 @@ def cpu_baseline(spec, lay):
     except Exception:  # noqa: BLE001
         cores = os.cpu_count()
     t0 = time.perf_counter()
-    fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M)
-    oracle.step_backward(fw, lay.X, lay.W)
+    fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M, hard=hard)
+    if spec.backward:
+        oracle.step_backward(fw, lay.X, lay.W)
     dt = time.perf_counter() - t0
     return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": "one full forward+backward step of the same %dx%d layer (T=%d), float64 NumPy, %.1f s"
-                      % (spec.cout, spec.cin, spec.T, dt)}
+            "sample": "one full %s step of the same %dx%d layer (T=%d), float64 NumPy, %.1f s"
+                      % ("forward+backward" if spec.backward else "forward", spec.cout, spec.cin, spec.T, dt)}
 
 
 def main():
@@ -162,7 +165,7 @@ def main():
     X = torch.from_numpy(lay.X).to(dev).to(tdt)
     logits = torch.from_numpy(lay.logits).to(dev)
     dlogits = torch.empty_like(logits)
-    sess = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, spec.N, spec.M)
+    sess = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, spec.N, spec.M, harden=args.harden)
     stream = torch.cuda.current_stream()
 
     def step(tf=None, tb=None):
@@ -207,7 +210,8 @@ def main():
                            "ms": round(bwd_gemm_ms if dom_name == "error_gemm" else fwd_gemm_ms, 4)}}
 
     if args.breakdown:
-        names = FWD_NAMES + (BWD_NAMES if spec.backward else [])
+        fwd_names = FWD_NAMES + (["harden"] if args.harden else [])
+        names = fwd_names + (BWD_NAMES if spec.backward else [])
         reps = 20
         evs = {n: [(he.new(), he.new()) for _ in range(reps)] for n in names}
         init_ev = [(ev(), ev()) for _ in range(reps)]
@@ -216,7 +220,7 @@ def main():
             init_ev[r][0].record(stream)
             sess.init()
             init_ev[r][1].record(stream)
-            tf = lcp.make_timing([_Ev(evs[n][r][0]) for n in FWD_NAMES], [_Ev(evs[n][r][1]) for n in FWD_NAMES])
+            tf = lcp.make_timing([_Ev(evs[n][r][0]) for n in fwd_names], [_Ev(evs[n][r][1]) for n in fwd_names])
             sess.forward(logits, timing=tf)
             if spec.backward:
                 tb = lcp.make_timing([_Ev(evs[n][r][0]) for n in BWD_NAMES],
@@ -231,10 +235,11 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, lay)
+        cpu = cpu_baseline(spec, lay, hard=args.harden)
 
     out = {
-        "metric": "LCP fwd+bwd steps/sec per layer (4096x11008, 2:4)",
+        "metric": "LCP %s steps/sec per layer (%dx%d, %d:%d)" % ("fwd+bwd" if spec.backward else "fwd",
+                                                                 spec.cout, spec.cin, spec.N, spec.M),
         "value": round(1000.0 / ms, 2),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -246,7 +251,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic (seeded LLaMA-shaped layer; no weights or calibration text available)",
-        "config": {"workload": "lcp_step_fwd_bwd", "layer": spec.name, "cout": spec.cout, "cin": spec.cin,
+        "config": {"workload": ("lcp_step_fwd_bwd" if spec.backward else "lcp_step_fwd")
+                               + ("_hardened" if args.harden else ""),
+                   "layer": spec.name, "cout": spec.cout, "cin": spec.cin,
                    "T": spec.T, "B": spec.B, "sinkhorn_iters": spec.iters, "tau": spec.tau,
                    "N": spec.N, "M": spec.M, "backward": spec.backward,
                    "includes_layer_setup": True},

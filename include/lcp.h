@@ -124,7 +124,8 @@ int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B,
  *   P: [nb][B][B] fp32 in (finite entries);
  *   P_hard (nullable): [nb][B][B] fp32 out, 1 where assigned, else 0;
  *   perm (nullable): [nb][B] int32 out, perm[b][k] = the row j assigned to
- *   column k. At least one output; P_hard must not alias P. B in {32,64,128}.
+ *   column k. At least one output; P_hard must not alias P; P and P_hard
+ *   16-byte aligned. B in {32,64,128}.
  */
 int lcp_harden(const float* P, int nb, int B, float* P_hard, int32_t* perm,
                void* stream);

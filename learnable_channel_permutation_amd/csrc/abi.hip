@@ -134,7 +134,7 @@ int lcp_harden(const float* P, int nb, int B, float* P_hard, int32_t* perm, void
   if (!P || nb <= 0 || B <= 0 || (!P_hard && !perm)) return LCP_E_INVAL;
   if (!good_B(B)) return LCP_E_UNSUPPORTED;
   if (!fits_i32(nb, (long long)B * B)) return LCP_E_INVAL;
-  if (P_hard == P) return LCP_E_INVAL;
+  if (P_hard == P || !aligned16(P) || (P_hard && !aligned16(P_hard))) return LCP_E_INVAL;
   LCP_RUN(launch_harden(P, nb, B, P_hard, perm, nullptr, nullptr, nullptr, S(stream)));
   return LCP_OK;
 }
