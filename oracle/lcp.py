@@ -36,7 +36,7 @@ __all__ = [
     "colnorm", "importance", "logsumexp", "sinkhorn", "block_permute",
     "nm_mask", "pack_bits", "unpack_bits", "unpermute_diff", "pruning_error",
     "step_forward", "step_backward", "sinkhorn_adjoint", "block_adjoint",
-    "harden",
+    "harden", "adamw", "tau_schedule", "train",
 ]
 
 
@@ -285,3 +285,43 @@ def harden(P):
         rows, cols = linear_sum_assignment(P[b], maximize=True)
         out[b, rows, cols] = 1.0
     return out
+
+
+# optimiser loop (implementation details of the PermLLM summary) -------------
+def adamw(param, grad, m, v, t, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
+    """One AdamW update (Loshchilov and Hutter: Adam with decoupled weight
+    decay) of step t >= 1. Returns (param, m, v):
+    m = b1 m + (1 - b1) g; v = b2 v + (1 - b2) g^2;
+    param <- param (1 - lr wd) - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)."""
+    g = _f64(grad)
+    m = beta1 * _f64(m) + (1.0 - beta1) * g
+    v = beta2 * _f64(v) + (1.0 - beta2) * g * g
+    mhat = m / (1.0 - beta1 ** t)
+    vhat = v / (1.0 - beta2 ** t)
+    p = _f64(param) * (1.0 - lr * weight_decay) - lr * mhat / (np.sqrt(vhat) + eps)
+    return p, m, v
+
+
+def tau_schedule(t, steps, tau0=1.0, tau1=0.1):
+    """Temperature of step t (0-based) of `steps`: linear from tau0 to tau1."""
+    if steps <= 1:
+        return float(tau0)
+    return float(tau0 + (tau1 - tau0) * t / (steps - 1))
+
+
+def train(W, X, logits, steps, lr, N, M, iters, hard=True, tau0=1.0, tau1=0.1, **adam):
+    """`steps` LCP steps on one layer: forward (hardened when `hard`), the
+    backward of E, one AdamW update of the logits, tau annealed linearly.
+    Returns (logits, list of E per step)."""
+    lg = _f64(logits).copy()
+    m = np.zeros_like(lg)
+    v = np.zeros_like(lg)
+    errs = []
+    for t in range(steps):
+        tau = tau_schedule(t, steps, tau0, tau1)
+        fw = step_forward(W, X, lg, tau, iters, N, M, hard=hard)
+        g = step_backward(fw, X, W)["dlogits"]
+        errs.append(fw["E"])
+        lg, m, v = adamw(lg, g, m, v, t + 1, lr, **adam)
+    return lg, errs
+

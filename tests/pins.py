@@ -538,6 +538,51 @@ def pin_straight_through_gradient_fd(o):
     assert err < 1e-6, err
 
 
+def pin_adamw_torch(o):
+    """AdamW against torch.optim.AdamW (CPU, float64) over several steps with
+    changing gradients."""
+    import torch
+    rng = _rng(26)
+    p0 = rng.standard_normal((3, 4, 4))
+    grads = [rng.standard_normal(p0.shape) for _ in range(5)]
+    for lr, wd in ((1e-3, 0.01), (5e-3, 0.1)):
+        tp = torch.tensor(p0.copy(), dtype=torch.float64, requires_grad=True)
+        opt = torch.optim.AdamW([tp], lr=lr, betas=(0.9, 0.999), eps=1e-8, weight_decay=wd)
+        p, m, v = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+        for t, g in enumerate(grads):
+            tp.grad = torch.tensor(g, dtype=torch.float64)
+            opt.step()
+            p, m, v = o.adamw(p, g, m, v, t + 1, lr, weight_decay=wd)
+        assert np.allclose(p, tp.detach().numpy(), rtol=1e-12, atol=1e-15), (lr, wd)
+
+
+def pin_tau_schedule(o):
+    """Linear temperature from 1 to 0.1 (PermLLM summary, implementation
+    details): endpoints and constant steps."""
+    assert o.tau_schedule(0, 11) == 1.0
+    assert abs(o.tau_schedule(10, 11) - 0.1) < 1e-15
+    steps = [o.tau_schedule(t, 11) for t in range(11)]
+    assert np.allclose(np.diff(steps), -0.09, rtol=0, atol=1e-15)
+
+
+def pin_training_beats_wanda(o):
+    """The method's claim on a seeded layer with an outlier-scaled X: after
+    AdamW training of the logits (hardened forward, straight-through
+    backward), the hard permutation prunes with less output error than plain
+    Wanda (identity permutation), and the loss has come down."""
+    rng = _rng(27)
+    cout, cin, T, B = 16, 32, 24, 8
+    W = rng.standard_normal((cout, cin)) * 0.02
+    X = rng.standard_normal((T, cin)) * np.exp(rng.standard_normal(cin))[None, :]
+    nb = cin // B
+    lg0 = 3.0 * np.eye(B)[None].repeat(nb, axis=0) + 1e-3 * rng.standard_normal((nb, B, B))
+    wanda = o.step_forward(W, X, None, 1.0, 5, 2, 4, P=np.eye(B)[None].repeat(nb, axis=0))["E"]
+    lg, errs = o.train(W, X, lg0, 60, 5e-2, 2, 4, 5, hard=True)
+    final = o.step_forward(W, X, lg, 0.1, 5, 2, 4, hard=True)["E"]
+    assert final < wanda, (final, wanda)
+    assert min(errs[-10:]) < errs[0], (errs[0], errs[-10:])
+
+
 ALL_PINS = [
     pin_sinkhorn_2x2_golden, pin_sinkhorn_uniform, pin_sinkhorn_closed_form,
     pin_sinkhorn_closed_form_values, pin_sinkhorn_doubly_stochastic,
@@ -548,5 +593,6 @@ ALL_PINS = [
     pin_identity_is_wanda, pin_hard_perm_error, pin_gram_identity,
     pin_cin8_enumeration, pin_step_gradient_fd, pin_block_adjoint_fd,
     pin_zero_error_gradient, pin_colnorm, pin_harden_bruteforce,
-    pin_hard_forward_planted, pin_straight_through_gradient_fd,
+    pin_hard_forward_planted, pin_straight_through_gradient_fd, pin_adamw_torch,
+    pin_tau_schedule, pin_training_beats_wanda,
 ]

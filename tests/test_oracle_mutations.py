@@ -168,6 +168,26 @@ def _ste_soft_in_block_adjoint(fw, X, W):
     return _orig["step_backward"](fw2, X, W)
 
 
+def _adamw_no_bias_correction(param, grad, m, v, t, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
+    g = np.asarray(grad, dtype=np.float64)
+    m = beta1 * np.asarray(m) + (1 - beta1) * g
+    v = beta2 * np.asarray(v) + (1 - beta2) * g * g
+    return np.asarray(param) * (1 - lr * weight_decay) - lr * m / (np.sqrt(v) + eps), m, v
+
+
+def _adamw_coupled_decay(param, grad, m, v, t, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
+    g = np.asarray(grad, dtype=np.float64) + weight_decay * np.asarray(param, dtype=np.float64)
+    return _orig["adamw"](param, g, m, v, t, lr, beta1, beta2, eps, 0.0)
+
+
+def _tau_reversed(t, steps, tau0=1.0, tau1=0.1):
+    return _orig["tau_schedule"](t, steps, tau1, tau0)
+
+
+def _train_soft(W, X, logits, steps, lr, N, M, iters, hard=True, **kw):
+    return _orig["train"](W, X, logits, steps, lr, N, M, iters, hard=False, **kw)
+
+
 MUTATIONS = [
     ("sinkhorn", _sinkhorn_cols_first),
     ("sinkhorn", _sinkhorn_times_tau),
@@ -197,6 +217,10 @@ MUTATIONS = [
     ("harden", _harden_transposed),
     ("step_backward", _ste_hard_in_sinkhorn_adjoint),
     ("step_backward", _ste_soft_in_block_adjoint),
+    ("adamw", _adamw_no_bias_correction),
+    ("adamw", _adamw_coupled_decay),
+    ("tau_schedule", _tau_reversed),
+    ("train", _train_soft),
 ]
 
 # the full 8! enumeration is covered by the plain pin run; the rest are fast
