@@ -218,6 +218,48 @@ int lcp_step_bwd(const lcp_layer* L, const float* logits, const lcp_cfg* c,
                  void* ws, size_t ws_bytes, float* dlogits,
                  const lcp_timing* tm, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Optimiser step on the logits: AdamW ([PermLLM] implementation details:
+ * AdamW, learning rate 1e-3 or 5e-3, temperature annealed linearly from 1 to
+ * 0.1 by the caller through lcp_cfg.tau). Decoupled weight decay (Loshchilov
+ * and Hutter): for step t >= 1,
+ *   m = b1 m + (1 - b1) g,  v = b2 v + (1 - b2) g^2,
+ *   p = p (1 - lr wd) - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+ * m and v are fp32 state owned by the caller (zero before step 1).
+ */
+typedef struct lcp_adamw_cfg {
+  float lr;            /* >= 0                                                  */
+  float beta1, beta2;  /* in [0, 1)                                             */
+  float eps;           /* > 0                                                   */
+  float weight_decay;  /* >= 0                                                  */
+} lcp_adamw_cfg;
+
+/* lcp_adamw - one update of n fp32 parameters from the gradient grad; param,
+ * m and v are updated in place (distinct buffers; grad may alias none). */
+int lcp_adamw(float* param, const float* grad, float* m, float* v, int n,
+              int t, const lcp_adamw_cfg* oc, void* stream);
+
+/* lcp_step_bwd_adamw - lcp_step_bwd followed by the AdamW update of the
+ * logits, fused into the Sinkhorn adjoint's last pass (the gradient is not
+ * written to memory unless dlogits is non-NULL). logits ([nb][B][B] fp32) is
+ * updated in place; m and v are [nb][B][B] fp32 state; all three 16-byte
+ * aligned and distinct. */
+int lcp_step_bwd_adamw(const lcp_layer* L, float* logits, const lcp_cfg* c,
+                       void* ws, size_t ws_bytes, float* m, float* v, int t,
+                       const lcp_adamw_cfg* oc, float* dlogits,
+                       const lcp_timing* tm, void* stream);
+
+/* lcp_train - `steps` optimisation steps of one layer's logits in place:
+ * for t = 0 .. steps-1, tau_t = tau0 + (tau1 - tau0) t / (steps - 1), then
+ * lcp_step_fwd (E written to errs[t], device fp32) and lcp_step_bwd_adamw
+ * with AdamW step t + 1. c->iters, N, M, harden apply to every step (the
+ * pages train with the hardened forward); c->tau is ignored. m, v: AdamW
+ * state as for lcp_step_bwd_adamw. Arguments are validated before the first
+ * step; a launch error stops the loop and is returned. */
+int lcp_train(const lcp_layer* L, float* logits, const lcp_cfg* c, void* ws,
+              size_t ws_bytes, float* m, float* v, int steps, float tau0,
+              float tau1, const lcp_adamw_cfg* oc, float* errs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,7 +13,8 @@ from . import _lib
 from ._lib import (LCP_BF16, LCP_F32, LcpError, lcp_colnorm, lcp_error,  # noqa: F401
                    lcp_error_workspace_bytes, lcp_harden, lcp_layer_init, lcp_nm_mask, lcp_permute,
                    lcp_sinkhorn, lcp_sinkhorn_bwd, lcp_step_bwd, lcp_step_fwd,
-                   lcp_step_workspace_bytes, lcp_xt_pitch, make_cfg, make_layer, make_timing)
+                   lcp_step_workspace_bytes, lcp_xt_pitch, make_cfg, make_layer, make_timing,
+                   lcp_adamw, lcp_step_bwd_adamw, lcp_train, make_adamw_cfg)
 
 __all__ = ["LayerSession", "LcpError"] + [n for n in _lib.EXPORTS if n.startswith("lcp_")]
 
@@ -59,3 +60,16 @@ class LayerSession:
             dlogits = torch.empty_like(logits)
         lcp_step_bwd(self.layer, logits, self.cfg, self.ws, dlogits, timing, stream)
         return dlogits
+
+    def train(self, logits, steps, lr, tau0=1.0, tau1=0.1, beta1=0.9, beta2=0.999, eps=1e-8,
+              weight_decay=0.01, stream=None):
+        """`steps` AdamW steps on `logits` (updated in place) with the
+        temperature annealed linearly from tau0 to tau1 (lcp_train). Returns
+        the per-step errors E as a device tensor."""
+        m = torch.zeros_like(logits)
+        v = torch.zeros_like(logits)
+        errs = torch.empty(steps, dtype=torch.float32, device=logits.device)
+        acfg = make_adamw_cfg(lr, beta1, beta2, eps, weight_decay)
+        lcp_train(self.layer, logits, self.cfg, self.ws, m, v, steps, tau0, tau1, acfg, errs, stream)
+        return errs
+

@@ -28,7 +28,7 @@ EXPORTS = [
     "lcp_status_string", "lcp_version", "lcp_sinkhorn", "lcp_sinkhorn_bwd", "lcp_colnorm",
     "lcp_xt_pitch", "lcp_layer_init", "lcp_permute", "lcp_nm_mask",
     "lcp_error_workspace_bytes", "lcp_error", "lcp_step_workspace_bytes", "lcp_step_fwd",
-    "lcp_step_bwd", "lcp_harden",
+    "lcp_step_bwd", "lcp_harden", "lcp_adamw", "lcp_step_bwd_adamw", "lcp_train",
 ]
 
 
@@ -41,6 +41,11 @@ class lcp_layer(ctypes.Structure):
 class lcp_cfg(ctypes.Structure):
     _fields_ = [("iters", ctypes.c_int), ("tau", ctypes.c_float), ("N", ctypes.c_int),
                 ("M", ctypes.c_int), ("harden", ctypes.c_int)]
+
+
+class lcp_adamw_cfg(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
 
 
 class lcp_timing(ctypes.Structure):
@@ -66,6 +71,11 @@ def _load():
         "lcp_sinkhorn": (i, [vp, vp, i, i, i, f, vp]),
         "lcp_sinkhorn_bwd": (i, [vp, vp, i, i, i, f, vp, vp]),
         "lcp_harden": (i, [vp, i, i, vp, vp, vp]),
+        "lcp_adamw": (i, [vp, vp, vp, vp, i, i, ctypes.POINTER(lcp_adamw_cfg), vp]),
+        "lcp_step_bwd_adamw": (i, [ctypes.POINTER(lcp_layer), vp, ctypes.POINTER(lcp_cfg), vp, sz, vp, vp, i,
+                                   ctypes.POINTER(lcp_adamw_cfg), vp, ctypes.POINTER(lcp_timing), vp]),
+        "lcp_train": (i, [ctypes.POINTER(lcp_layer), vp, ctypes.POINTER(lcp_cfg), vp, sz, vp, vp, i, f, f,
+                          ctypes.POINTER(lcp_adamw_cfg), vp, vp]),
         "lcp_colnorm": (i, [vp, i, i, i, vp, vp]),
         "lcp_xt_pitch": (i, [i]),
         "lcp_layer_init": (i, [vp, i, i, i, vp, vp, vp]),
@@ -132,6 +142,15 @@ def lcp_sinkhorn_bwd(logits, dP, iters, tau, dlogits, stream=None):
 def lcp_harden(P, P_hard=None, perm=None, stream=None):
     nb, B, _ = P.shape
     return _check("lcp_harden", LIB.lcp_harden(_p(P), nb, B, _p(P_hard), _p(perm), _stream(stream)))
+
+
+def make_adamw_cfg(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
+    return lcp_adamw_cfg(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay))
+
+
+def lcp_adamw(param, grad, m, v, t, cfg, stream=None):
+    return _check("lcp_adamw", LIB.lcp_adamw(_p(param), _p(grad), _p(m), _p(v), param.numel(), int(t),
+                                             ctypes.byref(cfg), _stream(stream)))
 
 
 def lcp_colnorm(X, norms, stream=None):
@@ -214,3 +233,19 @@ def lcp_step_bwd(layer, logits, cfg, ws, dlogits, timing=None, stream=None):
                                                    ws.numel() * ws.element_size(), _p(dlogits),
                                                    None if timing is None else ctypes.byref(timing),
                                                    _stream(stream)))
+
+
+def lcp_step_bwd_adamw(layer, logits, cfg, ws, m, v, t, acfg, dlogits=None, timing=None, stream=None):
+    return _check("lcp_step_bwd_adamw",
+                  LIB.lcp_step_bwd_adamw(ctypes.byref(layer), _p(logits), ctypes.byref(cfg), _p(ws),
+                                         ws.numel() * ws.element_size(), _p(m), _p(v), int(t), ctypes.byref(acfg),
+                                         _p(dlogits), None if timing is None else ctypes.byref(timing),
+                                         _stream(stream)))
+
+
+def lcp_train(layer, logits, cfg, ws, m, v, steps, tau0, tau1, acfg, errs, stream=None):
+    return _check("lcp_train", LIB.lcp_train(ctypes.byref(layer), _p(logits), ctypes.byref(cfg), _p(ws),
+                                             ws.numel() * ws.element_size(), _p(m), _p(v), int(steps),
+                                             float(tau0), float(tau1), ctypes.byref(acfg), _p(errs),
+                                             _stream(stream)))
+

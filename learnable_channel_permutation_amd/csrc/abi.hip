@@ -92,6 +92,68 @@ struct Timer {
 
 }  // namespace
 
+// AdamW arguments -> kernel parameters (bias corrections computed here).
+static int make_adamw(float* param, float* m, float* v, int t, const lcp_adamw_cfg* oc, AdamW* o) {
+  if (!param || !m || !v || !oc || t < 1) return LCP_E_INVAL;
+  if (param == m || param == v || m == v) return LCP_E_INVAL;
+  const bool ok = isfinite(oc->lr) && oc->lr >= 0.f && oc->beta1 >= 0.f && oc->beta1 < 1.f &&
+                  oc->beta2 >= 0.f && oc->beta2 < 1.f && isfinite(oc->eps) && oc->eps > 0.f &&
+                  isfinite(oc->weight_decay) && oc->weight_decay >= 0.f;
+  if (!ok) return LCP_E_INVAL;
+  const double bc1 = 1.0 - pow((double)oc->beta1, (double)t), bc2 = 1.0 - pow((double)oc->beta2, (double)t);
+  if (!(bc1 > 0.0) || !(bc2 > 0.0)) return LCP_E_INVAL;
+  *o = AdamW{param, m, v, oc->lr, oc->beta1, oc->beta2, oc->eps, oc->weight_decay, (float)bc1, (float)bc2};
+  return LCP_OK;
+}
+
+static int step_bwd_impl(const lcp_layer* L, const float* logits, const lcp_cfg* c, void* ws, size_t ws_bytes,
+                         float* dlogits, const AdamW* opt, const lcp_timing* tm, void* stream) {
+  int rc = check_step_args(L, logits, c);
+  if (rc != LCP_OK) return rc;
+  if (dlogits && !aligned16(dlogits)) return LCP_E_INVAL;
+  const bool bf = L->dtype == LCP_BF16;
+  if (bf && (!L->Xt || !aligned16(L->Xt))) return LCP_E_INVAL;
+  const StepLayout Ly = step_layout(L->cout, L->cin, L->T, L->B, c->iters, L->dtype);
+  rc = check_ws(ws, ws_bytes, Ly.total);
+  if (rc != LCP_OK) return rc;
+
+  char* base = (char*)ws;
+  // the block adjoint is taken at the P the forward used (the hard P when
+  // hardened: straight-through, the Sinkhorn adjoint below stays soft)
+  const float* P = (const float*)(base + (c->harden ? Ly.Ph : Ly.P));
+  const float* off = (const float*)(base + Ly.off);
+  const uint32_t* bits = (const uint32_t*)(base + Ly.bits);
+  void* Gd = base + Ly.D;           // G reuses the forward's D buffer
+  const void* R = base + Ly.R;
+  const float* Ews = (const float*)(base + Ly.E);
+  float* adj = (float*)(base + Ly.adj);
+  hipStream_t s = S(stream);
+  const Timer tmr{tm, s};
+
+  tmr.start(0);
+  if (bf)
+    LCP_RUN(launch_gemm_dd_bf16((const uint16_t*)R, Ly.pitch, (const uint16_t*)L->Xt, Ly.pitch, L->cout, L->cin,
+                                Ly.pitch, Ews, (uint16_t*)Gd, L->cin, s));
+  else
+    LCP_RUN(launch_gemm_dd_f32((const float*)R, Ly.pitch, (const float*)L->X, L->cin, L->cout, L->cin, L->T, Ews,
+                               (float*)Gd, L->cin, s));
+  tmr.stop(0);
+  const u32x4* fragA = (const u32x4*)(base + Ly.fragA);
+  tmr.start(1);
+  if (bf)
+    LCP_RUN(launch_adjoint_bf16((const uint16_t*)Gd, (const uint16_t*)L->W, fragA, P, bits, L->cout, L->cin,
+                                L->B, Ly.sp, adj, s));
+  else
+    LCP_RUN(launch_adjoint_f32((const float*)Gd, (const float*)L->W, P, bits, L->cout, L->cin, L->B, Ly.sp,
+                               adj, s));
+  tmr.stop(1);
+  tmr.start(2);
+  LCP_RUN(launch_sinkhorn_bwd(logits, adj, &Ly.sp, off, dlogits, Ly.nb, L->B, c->iters, c->tau, opt, s));
+  tmr.stop(2);
+  return LCP_OK;
+}
+
+
 extern "C" {
 
 const char* lcp_status_string(int code) {
@@ -126,7 +188,7 @@ int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B, int it
   if ((long long)iters * B > kMaxIterB) return LCP_E_UNSUPPORTED;
   if (!fits_i32(nb, (long long)B * B) || !aligned16(logits) || !aligned16(dP) || !aligned16(dlogits))
     return LCP_E_INVAL;
-  LCP_RUN(launch_sinkhorn_bwd(logits, dP, nullptr, nullptr, dlogits, nb, B, iters, tau, S(stream)));
+  LCP_RUN(launch_sinkhorn_bwd(logits, dP, nullptr, nullptr, dlogits, nb, B, iters, tau, nullptr, S(stream)));
   return LCP_OK;
 }
 
@@ -309,48 +371,60 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
 
 int lcp_step_bwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void* ws, size_t ws_bytes,
                  float* dlogits, const lcp_timing* tm, void* stream) {
-  int rc = check_step_args(L, logits, c);
+  if (!dlogits) return LCP_E_INVAL;
+  return step_bwd_impl(L, logits, c, ws, ws_bytes, dlogits, nullptr, tm, stream);
+}
+
+int lcp_adamw(float* param, const float* grad, float* m, float* v, int n, int t, const lcp_adamw_cfg* oc,
+              void* stream) {
+  AdamW o;
+  int rc = make_adamw(param, m, v, t, oc, &o);
   if (rc != LCP_OK) return rc;
-  if (!dlogits || !aligned16(dlogits)) return LCP_E_INVAL;
-  const bool bf = L->dtype == LCP_BF16;
-  if (bf && (!L->Xt || !aligned16(L->Xt))) return LCP_E_INVAL;
+  if (!grad || n <= 0) return LCP_E_INVAL;
+  LCP_RUN(launch_adamw(grad, n, o, S(stream)));
+  return LCP_OK;
+}
+
+int lcp_step_bwd_adamw(const lcp_layer* L, float* logits, const lcp_cfg* c, void* ws, size_t ws_bytes,
+                       float* m, float* v, int t, const lcp_adamw_cfg* oc, float* dlogits,
+                       const lcp_timing* tm, void* stream) {
+  AdamW o;
+  int rc = make_adamw(logits, m, v, t, oc, &o);
+  if (rc != LCP_OK) return rc;
+  if (!aligned16(logits) || !aligned16(m) || !aligned16(v)) return LCP_E_INVAL;
+  if (dlogits == logits || dlogits == m || dlogits == v) return LCP_E_INVAL;
+  return step_bwd_impl(L, logits, c, ws, ws_bytes, dlogits, &o, tm, stream);
+}
+
+int lcp_train(const lcp_layer* L, float* logits, const lcp_cfg* c, void* ws, size_t ws_bytes, float* m,
+              float* v, int steps, float tau0, float tau1, const lcp_adamw_cfg* oc, float* errs,
+              void* stream) {
+  if (!c || steps < 1 || !good_tau(tau0) || !good_tau(tau1)) return LCP_E_INVAL;
+  if (!errs) return LCP_E_INVAL;
+  lcp_cfg cs = *c;
+  // validate everything once with the first step's arguments (nothing is
+  // enqueued on an error)
+  cs.tau = tau0;
+  int rc = check_step_args(L, logits, &cs);
+  if (rc != LCP_OK) return rc;
+  AdamW probe;
+  rc = make_adamw(logits, m, v, steps, oc, &probe);
+  if (rc != LCP_OK) return rc;
+  rc = make_adamw(logits, m, v, 1, oc, &probe);
+  if (rc != LCP_OK) return rc;
   const StepLayout Ly = step_layout(L->cout, L->cin, L->T, L->B, c->iters, L->dtype);
   rc = check_ws(ws, ws_bytes, Ly.total);
   if (rc != LCP_OK) return rc;
-
-  char* base = (char*)ws;
-  // the block adjoint is taken at the P the forward used (the hard P when
-  // hardened: straight-through, the Sinkhorn adjoint below stays soft)
-  const float* P = (const float*)(base + (c->harden ? Ly.Ph : Ly.P));
-  const float* off = (const float*)(base + Ly.off);
-  const uint32_t* bits = (const uint32_t*)(base + Ly.bits);
-  void* Gd = base + Ly.D;           // G reuses the forward's D buffer
-  const void* R = base + Ly.R;
-  const float* Ews = (const float*)(base + Ly.E);
-  float* adj = (float*)(base + Ly.adj);
-  hipStream_t s = S(stream);
-  const Timer tmr{tm, s};
-
-  tmr.start(0);
-  if (bf)
-    LCP_RUN(launch_gemm_dd_bf16((const uint16_t*)R, Ly.pitch, (const uint16_t*)L->Xt, Ly.pitch, L->cout, L->cin,
-                                Ly.pitch, Ews, (uint16_t*)Gd, L->cin, s));
-  else
-    LCP_RUN(launch_gemm_dd_f32((const float*)R, Ly.pitch, (const float*)L->X, L->cin, L->cout, L->cin, L->T, Ews,
-                               (float*)Gd, L->cin, s));
-  tmr.stop(0);
-  const u32x4* fragA = (const u32x4*)(base + Ly.fragA);
-  tmr.start(1);
-  if (bf)
-    LCP_RUN(launch_adjoint_bf16((const uint16_t*)Gd, (const uint16_t*)L->W, fragA, P, bits, L->cout, L->cin,
-                                L->B, Ly.sp, adj, s));
-  else
-    LCP_RUN(launch_adjoint_f32((const float*)Gd, (const float*)L->W, P, bits, L->cout, L->cin, L->B, Ly.sp,
-                               adj, s));
-  tmr.stop(1);
-  tmr.start(2);
-  LCP_RUN(launch_sinkhorn_bwd(logits, adj, &Ly.sp, off, dlogits, Ly.nb, L->B, c->iters, c->tau, s));
-  tmr.stop(2);
+  if (L->dtype == LCP_BF16 && (!L->Xt || !aligned16(L->Xt))) return LCP_E_INVAL;
+  if (!aligned16(m) || !aligned16(v)) return LCP_E_INVAL;
+  for (int t = 0; t < steps; ++t) {
+    // temperature linear from tau0 (first step) to tau1 (last step)
+    cs.tau = (float)((double)tau0 + ((double)tau1 - tau0) * (steps > 1 ? (double)t / (steps - 1) : 0.0));
+    rc = lcp_step_fwd(L, logits, &cs, ws, ws_bytes, errs + t, nullptr, nullptr, nullptr, stream);
+    if (rc != LCP_OK) return rc;
+    rc = lcp_step_bwd_adamw(L, logits, &cs, ws, ws_bytes, m, v, t + 1, oc, nullptr, nullptr, stream);
+    if (rc != LCP_OK) return rc;
+  }
   return LCP_OK;
 }
 

@@ -23,11 +23,23 @@ struct AdjSplit {
 hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb, int B,
                                int iters, float tau, const float* n, u32x4* fwd, u32x4* adj,
                                hipStream_t s);
+// AdamW update applied to the logits (state m, v in fp32); bc1 = 1 - b1^t,
+// bc2 = 1 - b2^t for step t.
+struct AdamW {
+  float* param;
+  float* m;
+  float* v;
+  float lr, b1, b2, eps, wd, bc1, bc2;
+};
 // dP is either dense [nb][B][B] (seg == nullptr) or the block adjoint's
 // (workgroup, segment) partials described by seg, summed in workgroup order.
+// dlogits may be null when opt is given; with opt the kernel also applies
+// AdamW to opt->param (the logits themselves, updated in place).
 hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, const AdjSplit* seg,
                                const float* off, float* dlogits, int nb, int B, int iters,
-                               float tau, hipStream_t s);
+                               float tau, const AdamW* opt, hipStream_t s);
+// Standalone AdamW over n elements.
+hipError_t launch_adamw(const float* grad, int n, const AdamW& opt, hipStream_t s);
 
 // Hardening (harden.hip): per block the permutation maximising Tr(P^T P_hat).
 // Any of P_hard ([nb][B][B] 0/1 fp32), perm ([nb][B]: source row of each

@@ -179,9 +179,9 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
 // 2 * iters * B floats.
 template <int B>
 __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
-    const float* __restrict__ logits, const float* __restrict__ dP, int seg_tpw, int seg_tpb,
+    const float* logits, const float* __restrict__ dP, int seg_tpw, int seg_tpb,
     int seg_maxseg, int seg_grid, const float* __restrict__ off, float* __restrict__ dlogits, int iters,
-    float scale, float inv_tau) {
+    float scale, float inv_tau, AdamW opt) {
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
   extern __shared__ float sh_off[];          // [iters][2][B]
@@ -317,14 +317,53 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
     }
   }
 
-  float* dst = dlogits + (size_t)b * B * B;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    float v[CPL];
+    const size_t o = (size_t)b * B * B + (row0 + a) * B + lc * CPL;
+    float gr[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = g[a][c] * inv_tau;
-    st_cols<CPL>(dst + (row0 + a) * B + lc * CPL, v);
+    for (int c = 0; c < CPL; ++c) gr[c] = g[a][c] * inv_tau;
+    if (dlogits != nullptr) st_cols<CPL>(dlogits + o, gr);
+    if (opt.param != nullptr) {
+      // AdamW on this lane's logits: the block's values were read at the
+      // start by this same lane, so the in-place update is race-free. No
+      // contraction: the same rounded operations as adamw_kernel.
+#pragma clang fp contract(off)
+      float p[CPL], mm[CPL], vv[CPL];
+      ld_cols<CPL>(opt.param + o, p);
+      ld_cols<CPL>(opt.m + o, mm);
+      ld_cols<CPL>(opt.v + o, vv);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        mm[c] = opt.b1 * mm[c] + (1.f - opt.b1) * gr[c];
+        vv[c] = opt.b2 * vv[c] + (1.f - opt.b2) * gr[c] * gr[c];
+        const float step = (mm[c] / opt.bc1) / (__builtin_sqrtf(vv[c] / opt.bc2) + opt.eps);
+        p[c] = p[c] * (1.f - opt.lr * opt.wd) - opt.lr * step;
+      }
+      st_cols<CPL>(opt.m + o, mm);
+      st_cols<CPL>(opt.v + o, vv);
+      st_cols<CPL>(opt.param + o, p);
+    }
   }
+}
+
+// Standalone AdamW, the same arithmetic as the fused epilogue above.
+__global__ __launch_bounds__(256) void adamw_kernel(const float* __restrict__ grad, int n, AdamW opt) {
+#pragma clang fp contract(off)
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float gr = grad[i];
+  const float mm = opt.b1 * opt.m[i] + (1.f - opt.b1) * gr;
+  const float vv = opt.b2 * opt.v[i] + (1.f - opt.b2) * gr * gr;
+  const float step = (mm / opt.bc1) / (__builtin_sqrtf(vv / opt.bc2) + opt.eps);
+  opt.m[i] = mm;
+  opt.v[i] = vv;
+  opt.param[i] = opt.param[i] * (1.f - opt.lr * opt.wd) - opt.lr * step;
+}
+
+hipError_t launch_adamw(const float* grad, int n, const AdamW& opt, hipStream_t s) {
+  adamw_kernel<<<(n + 255) / 256, 256, 0, s>>>(grad, n, opt);
+  return hipGetLastError();
 }
 
 // ---- launchers ---------------------------------------------------------------
@@ -346,16 +385,17 @@ hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb
 
 hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, const AdjSplit* seg,
                                const float* off, float* dlogits, int nb, int B, int iters,
-                               float tau, hipStream_t s) {
+                               float tau, const AdamW* opt, hipStream_t s) {
+  const AdamW o = opt ? *opt : AdamW{nullptr, nullptr, nullptr, 0.f, 0.f, 0.f, 0.f, 0.f, 1.f, 1.f};
   const int tpw = seg ? seg->tpw : 0, tpb = seg ? seg->tpb : 0;
   const int maxseg = seg ? seg->maxseg : 0, grid = seg ? seg->grid : 0;
   const float scale = sk_scale(tau);
   const float inv_tau = (float)(1.0 / (double)tau);
   const size_t lds = (size_t)iters * 2 * B * sizeof(float);
   switch (B) {
-    case 32: sinkhorn_bwd_kernel<32><<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau); break;
-    case 64: sinkhorn_bwd_kernel<64><<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau); break;
-    case 128: sinkhorn_bwd_kernel<128><<<nb, SkGeom<128>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau); break;
+    case 32: sinkhorn_bwd_kernel<32><<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau, o); break;
+    case 64: sinkhorn_bwd_kernel<64><<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau, o); break;
+    case 128: sinkhorn_bwd_kernel<128><<<nb, SkGeom<128>::THREADS, lds, s>>>(logits, dP, tpw, tpb, maxseg, grid, off, dlogits, iters, scale, inv_tau, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
