@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
     ap.add_argument("--harden", action="store_true",
                     help="hardened forward + straight-through backward (another workload)")
+    ap.add_argument("--adamw", action="store_true",
+                    help="training step: the backward with the fused AdamW update of the logits")
+    ap.add_argument("--saturate", action="store_true",
+                    help="also time the Sinkhorn and the N:M mask at saturating sizes (to stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (HBM counter calibration)")
@@ -88,6 +92,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.made = []
 
     def new(self):
@@ -96,6 +101,10 @@ class HipEvents:
             raise RuntimeError("hipEventCreate failed")
         self.made.append(e)
         return e
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def ms(self, a, b):
         out = self.ct.c_float()
@@ -136,6 +145,44 @@ def cpu_baseline(spec, lay, hard=False):
                       % ("forward+backward" if spec.backward else "forward", spec.cout, spec.cin, spec.T, dt)}
 
 
+def saturating_kernels(lcp, torch, he):
+    """Sinkhorn forward over all B = 64 blocks of a LLaMA-7B-shaped model's
+    projection layers (17,792 blocks) and lcp_nm_mask on 28672 x 8192 fp32
+    scores, timed with HIP events; HBM bytes are the algorithmic ones (inputs
+    read once, outputs written once)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    out = {}
+    nb, B, L = 17792, 64, 5
+    rng = np.random.Generator(np.random.PCG64(99))
+    lg = torch.from_numpy((3.0 * np.eye(B, dtype=np.float32)[None] +
+                           1e-3 * rng.standard_normal((1, B, B)).astype(np.float32)).repeat(nb, axis=0)).to(dev)
+    P = torch.empty_like(lg)
+    rows, cin = 28672, 8192
+    scores = torch.rand((rows, cin), dtype=torch.float32, device=dev)
+    bits = torch.empty((rows, cin // 32), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        lcp.lcp_sinkhorn(lg, P, L, 1.0)
+        lcp.lcp_nm_mask(scores, 2, 4, bits)
+    torch.cuda.synchronize()
+    reps = 10
+    for name, fn, nbytes in (
+            ("sinkhorn_fwd_17792x64x64", lambda: lcp.lcp_sinkhorn(lg, P, L, 1.0), 2 * nb * B * B * 4),
+            ("nm_mask_28672x8192", lambda: lcp.lcp_nm_mask(scores, 2, 4, bits), rows * cin * 4 + rows * cin // 8)):
+        evs = [(he.new(), he.new()) for _ in range(reps)]
+        st = torch.cuda.current_stream()
+        for a, b in evs:
+            he.record(a, st)
+            fn()
+            he.record(b, st)
+        torch.cuda.synchronize()
+        ms = sum(he.ms(a, b) for a, b in evs) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 1), "GB_per_s": round(gbs, 1), "frac_of_8TBs": round(gbs / 8000.0, 3),
+                     "bytes": nbytes}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,10 +215,19 @@ def main():
     sess = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, spec.N, spec.M, harden=args.harden)
     stream = torch.cuda.current_stream()
 
+    m_state = torch.zeros_like(logits)
+    v_state = torch.zeros_like(logits)
+    acfg = lcp.make_adamw_cfg(5e-3)
+    t_opt = [0]
+
     def step(tf=None, tb=None):
         sess.init()
         sess.forward(logits, timing=tf)
-        if spec.backward:
+        if spec.backward and args.adamw:
+            t_opt[0] += 1
+            lcp.lcp_step_bwd_adamw(sess.layer, logits, sess.cfg, sess.ws, m_state, v_state, t_opt[0], acfg,
+                                   timing=tb)
+        elif spec.backward:
             sess.backward(logits, dlogits, timing=tb)
 
     for _ in range(args.warmup):
@@ -231,6 +287,9 @@ def main():
         print("  %-24s %8.4f" % ("layer_init", sum(a.elapsed_time(b) for a, b in init_ev) / reps), file=sys.stderr)
         for n in names:
             print("  %-24s %8.4f" % (n, sum(he.ms(a, b) for a, b in evs[n]) / reps), file=sys.stderr)
+    if args.saturate:
+        sat = saturating_kernels(lcp, torch, he)
+        print("saturating sizes: " + json.dumps(sat), file=sys.stderr)
     he.close()
 
     cpu = None
@@ -252,7 +311,8 @@ def main():
         "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic (seeded LLaMA-shaped layer; no weights or calibration text available)",
         "config": {"workload": ("lcp_step_fwd_bwd" if spec.backward else "lcp_step_fwd")
-                               + ("_hardened" if args.harden else ""),
+                               + ("_hardened" if args.harden else "")
+                               + ("_adamw" if (args.adamw and spec.backward) else ""),
                    "layer": spec.name, "cout": spec.cout, "cin": spec.cin,
                    "T": spec.T, "B": spec.B, "sinkhorn_iters": spec.iters, "tau": spec.tau,
                    "N": spec.N, "M": spec.M, "backward": spec.backward,
