@@ -19,7 +19,16 @@ design notes):
   E = ||(W - W_tilde) X^T||_F (not squared, not normalised). The task
   definition asks for the permuted, pruned weight closest to the dense one on
   the layer's outputs; this is that distance.
-* The mask is held constant in the backward pass (no straight-through term).
+* By default the mask is held constant in the backward pass. With mask_ste
+  the gradient that reaches the 0/1 mask is handed unchanged to the permuted
+  scores S_hat = S P_B (straight-through estimator for the argmax that picks
+  the mask, PermLLM summary, integration with pruning methods), which adds
+  S_b^T ((G_b P_b) . (W_b P_b)) to d/dP_b.
+* The cosine objective (PermLLM summary, optimisation objective) compares the
+  dense outputs y = W X^T with the sparse outputs y~ = W_tilde X^T over the
+  whole output tensor, flattened into one vector per layer:
+  L = 1 - <y, y~> / (||y|| ||y~||). When either norm is zero the loss is 1
+  and its gradient zero.
 * Hardening (Method 2) is optional: the forward may replace P_hat by the
   permutation maximising Tr(P^T P_hat) per block; the backward then takes the
   block adjoint at the hard P and passes it unchanged to the adjoint of the
@@ -36,7 +45,8 @@ __all__ = [
     "colnorm", "importance", "logsumexp", "sinkhorn", "block_permute",
     "nm_mask", "pack_bits", "unpack_bits", "unpermute_diff", "pruning_error",
     "step_forward", "step_backward", "sinkhorn_adjoint", "block_adjoint",
-    "harden", "adamw", "tau_schedule", "train",
+    "harden", "adamw", "tau_schedule", "train", "layer_output", "cosine_loss",
+    "cosine_grad", "mask_ste_adjoint",
 ]
 
 
@@ -186,15 +196,20 @@ def pruning_error(D, X):
 
 
 # forward step ---------------------------------------------------------------
-def step_forward(W, X, logits, tau, iters, N, M, P=None, mask=None, hard=False):
+def step_forward(W, X, logits, tau, iters, N, M, P=None, mask=None, hard=False,
+                 loss="frobenius"):
     """One LCP forward step (O1 .. O7). Returns a dict of every intermediate.
 
     P overrides the Sinkhorn output (used to feed hard permutations); mask
     overrides the N:M selection (used to freeze the mask for finite
-    differences). hard=True replaces the soft P_hat by its hardened
-    permutation before the block permutation (PermLLM summary, Method 2); the
-    dict then holds the hard matrix as "P" and the Sinkhorn output as
-    "P_soft"."""
+    differences; any real array is accepted). hard=True replaces the soft
+    P_hat by its hardened permutation before the block permutation (PermLLM
+    summary, Method 2); the dict then holds the hard matrix as "P" and the
+    Sinkhorn output as "P_soft". "L" is the objective named by `loss`:
+    "frobenius" (L = E) or "cosine" (L = cosine_loss of the dense and sparse
+    outputs, which are then returned as "Y" and "Y_tilde")."""
+    if loss not in ("frobenius", "cosine"):
+        raise ValueError("unknown loss %r" % (loss,))
     W = _f64(W)
     X = _f64(X)
     n = colnorm(X)
@@ -212,9 +227,15 @@ def step_forward(W, X, logits, tau, iters, N, M, P=None, mask=None, hard=False):
         mask = nm_mask(S_hat, N, M)
     A, W_tilde, D = unpermute_diff(W, W_hat, mask, P)
     R, E = pruning_error(D, X)
-    return {"n": n, "S": S, "P": P, "P_soft": P_soft, "hard": bool(hard), "trace": tr,
-            "W_hat": W_hat, "S_hat": S_hat, "mask": mask, "A": A, "W_tilde": W_tilde,
-            "D": D, "R": R, "E": E, "tau": float(tau), "iters": int(iters)}
+    out = {"n": n, "S": S, "P": P, "P_soft": P_soft, "hard": bool(hard), "trace": tr,
+           "W_hat": W_hat, "S_hat": S_hat, "mask": mask, "A": A, "W_tilde": W_tilde,
+           "D": D, "R": R, "E": E, "tau": float(tau), "iters": int(iters), "loss": loss,
+           "L": E}
+    if loss == "cosine":
+        Y = layer_output(W, X)
+        Yt = layer_output(W_tilde, X)
+        out.update(Y=Y, Y_tilde=Yt, L=cosine_loss(Y, Yt))
+    return out
 
 
 # O8 .. O10 ------------------------------------------------------------------
@@ -253,24 +274,85 @@ def sinkhorn_adjoint(dP, P, trace, tau):
     return G / float(tau)
 
 
-def step_backward(fw, X, W):
-    """Gradient of E with respect to the logits (O8 .. O11), mask constant.
+def step_backward(fw, X, W, mask_ste=False):
+    """Gradient of the forward's objective L with respect to the logits
+    (O8 .. O11).
 
-    dR = R / E (zero when E = 0); G = dE/dW_tilde = -dR X; then the block
-    adjoint and the Sinkhorn adjoint. Requires a forward dict whose P came
+    Frobenius: dR = R / E (zero when E = 0) and G = dL/dW_tilde = -dR X.
+    Cosine: G = (dL/dY~) X with dL/dY~ from cosine_grad. Then the block
+    adjoint (mask constant), plus the mask's straight-through term when
+    mask_ste, and the Sinkhorn adjoint. Requires a forward dict whose P came
     from the Sinkhorn (trace present). For a hardened forward the block
     adjoint is taken at the hard P and its result is handed unchanged to the
     Sinkhorn adjoint of the soft P_hat (straight-through estimator, PermLLM
     summary, Method 2)."""
     if fw["trace"] is None:
         raise ValueError("forward step must come from logits")
-    E = fw["E"]
-    R = fw["R"]
-    dR = R / E if E > 0 else np.zeros_like(R)
-    G = -(dR @ _f64(X))
+    out = {}
+    if fw["loss"] == "cosine":
+        dYt = cosine_grad(fw["Y"], fw["Y_tilde"])
+        G = dYt @ _f64(X)
+        out["dYt"] = dYt
+    else:
+        E = fw["E"]
+        R = fw["R"]
+        dR = R / E if E > 0 else np.zeros_like(R)
+        G = -(dR @ _f64(X))
+        out["dR"] = dR
     dP = block_adjoint(G, fw["A"], W, fw["P"], fw["mask"])
+    if mask_ste:
+        dP = dP + mask_ste_adjoint(G, W, fw["S"], fw["P"])
     dL = sinkhorn_adjoint(dP, fw["P_soft"], fw["trace"], fw["tau"])
-    return {"dR": dR, "G": G, "dP": dP, "dlogits": dL}
+    out.update(G=G, dP=dP, dlogits=dL)
+    return out
+
+
+# cosine objective and the mask's straight-through term ----------------------
+def layer_output(W, X):
+    """Y = W X^T (Cout x T): the layer's outputs on the T calibration tokens,
+    one column per token."""
+    return _f64(W) @ _f64(X).T
+
+
+def cosine_loss(Y, Yt):
+    """L = 1 - <y, y~> / (||y|| ||y~||) (PermLLM summary, optimisation
+    objective) with y, y~ the flattened arrays; 1 when either norm is 0."""
+    y = _f64(Y).ravel()
+    yt = _f64(Yt).ravel()
+    ny = np.sqrt(np.dot(y, y))
+    nt = np.sqrt(np.dot(yt, yt))
+    if ny == 0.0 or nt == 0.0:
+        return 1.0
+    return float(1.0 - np.dot(y, yt) / (ny * nt))
+
+
+def cosine_grad(Y, Yt):
+    """dL/dY~ of cosine_loss: -Y / (|Y| |Y~|) + <Y, Y~> Y~ / (|Y| |Y~|^3)
+    (the quotient rule on the definition); zero when either norm is 0."""
+    Y = _f64(Y)
+    Yt = _f64(Yt)
+    ny = np.sqrt(np.sum(Y * Y))
+    nt = np.sqrt(np.sum(Yt * Yt))
+    if ny == 0.0 or nt == 0.0:
+        return np.zeros_like(Yt)
+    p = np.sum(Y * Yt)
+    return -Y / (ny * nt) + p * Yt / (ny * nt ** 3)
+
+
+def mask_ste_adjoint(G, W, S, P):
+    """Straight-through term of the N:M mask (PermLLM summary, integration
+    with pruning methods: the argmax that picks the mask is passed through by
+    the STE). A = W_hat . M gives dL/dM = dL/dA . W_hat = (G_b P_b) . W_hat_b;
+    passed unchanged to S_hat_b = S_b P_b it contributes S_b^T dL/dM_b to
+    dL/dP_b. G = dL/dW_tilde, S the unpermuted importance."""
+    P = _f64(P)
+    nb, B, _ = P.shape
+    rows = G.shape[0]
+    Gb = _f64(G).reshape(rows, nb, B).transpose(1, 0, 2)
+    Wb = _f64(W).reshape(rows, nb, B).transpose(1, 0, 2)
+    Sb = _f64(S).reshape(rows, nb, B).transpose(1, 0, 2)
+    dM = np.matmul(Gb, P) * np.matmul(Wb, P)
+    return np.matmul(Sb.transpose(0, 2, 1), dM)
 
 
 # hardening (Method 2) -------------------------------------------------------
@@ -309,19 +391,21 @@ def tau_schedule(t, steps, tau0=1.0, tau1=0.1):
     return float(tau0 + (tau1 - tau0) * t / (steps - 1))
 
 
-def train(W, X, logits, steps, lr, N, M, iters, hard=True, tau0=1.0, tau1=0.1, **adam):
+def train(W, X, logits, steps, lr, N, M, iters, hard=True, tau0=1.0, tau1=0.1,
+          loss="frobenius", mask_ste=False, **adam):
     """`steps` LCP steps on one layer: forward (hardened when `hard`), the
-    backward of E, one AdamW update of the logits, tau annealed linearly.
-    Returns (logits, list of E per step)."""
+    backward of the objective `loss` (with the mask's straight-through term
+    when `mask_ste`), one AdamW update of the logits, tau annealed linearly.
+    Returns (logits, list of the objective per step)."""
     lg = _f64(logits).copy()
     m = np.zeros_like(lg)
     v = np.zeros_like(lg)
     errs = []
     for t in range(steps):
         tau = tau_schedule(t, steps, tau0, tau1)
-        fw = step_forward(W, X, lg, tau, iters, N, M, hard=hard)
-        g = step_backward(fw, X, W)["dlogits"]
-        errs.append(fw["E"])
+        fw = step_forward(W, X, lg, tau, iters, N, M, hard=hard, loss=loss)
+        g = step_backward(fw, X, W, mask_ste=mask_ste)["dlogits"]
+        errs.append(fw["L"])
         lg, m, v = adamw(lg, g, m, v, t + 1, lr, **adam)
     return lg, errs
 

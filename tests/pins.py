@@ -583,6 +583,150 @@ def pin_training_beats_wanda(o):
     assert min(errs[-10:]) < errs[0], (errs[0], errs[-10:])
 
 
+# ------------------------------------------------- cosine objective, mask STE --
+def pin_cosine_closed_forms(o):
+    """Cosine loss (PermLLM summary, optimisation objective) on vectors whose
+    angle is known, its invariance to scaling y~, the zero-norm convention,
+    and scipy's cosine distance (a library routine of the same definition)
+    on flattened random matrices."""
+    from scipy.spatial.distance import cosine
+    assert abs(o.cosine_loss([[1.0, 0.0]], [[1.0, 1.0]]) - (1 - 1 / math.sqrt(2))) < 1e-15
+    assert abs(o.cosine_loss([[3.0, 4.0]], [[4.0, -3.0]]) - 1.0) < 1e-15
+    assert abs(o.cosine_loss([[1.0, 2.0]], [[-2.0, -4.0]]) - 2.0) < 1e-15
+    assert abs(o.cosine_loss([[1.0, 2.0]], [[2.0, 4.0]])) < 1e-15
+    rng = _rng(28)
+    Y = rng.standard_normal((5, 7))
+    Yt = Y + 0.3 * rng.standard_normal((5, 7))
+    want = cosine(Y.ravel(), Yt.ravel())
+    assert abs(o.cosine_loss(Y, Yt) - want) < 1e-14
+    assert abs(o.cosine_loss(Y, 2.5 * Yt) - want) < 1e-14
+    assert abs(o.cosine_loss(Y.T, Yt.T) - want) < 1e-14
+    assert o.cosine_loss(Y, np.zeros_like(Y)) == 1.0
+
+
+def pin_cosine_dense_is_zero(o):
+    """All-ones mask and a hard P: the sparse layer is the dense one, so the
+    cosine loss is 0; with the N:M mask it is positive."""
+    rng = _rng(29)
+    cout, cin, T, B = 6, 16, 9, 8
+    W = rng.standard_normal((cout, cin))
+    X = rng.standard_normal((T, cin))
+    nb = cin // B
+    Pi = np.zeros((nb, B, B))
+    for b in range(nb):
+        Pi[b, np.arange(B), rng.permutation(B)] = 1.0
+    lg = 2.0 * Pi + 0.05 * rng.standard_normal((nb, B, B))
+    ones = np.ones((cout, cin))
+    fw = o.step_forward(W, X, lg, 1.0, 3, 2, 4, hard=True, mask=ones, loss="cosine")
+    assert abs(fw["L"]) < 1e-14, fw["L"]
+    fs = o.step_forward(W, X, lg, 1.0, 3, 2, 4, hard=True, loss="cosine")
+    assert fs["L"] > 1e-3, fs["L"]
+
+
+def pin_cosine_gradient_fd(o):
+    """d L_cos / d logits against central differences with the mask frozen."""
+    for seed, kw in ((30, {}), (31, {"B": 8, "N": 4, "M": 8, "L": 3, "tau": 1.3})):
+        W, X, lg, tau, L, N, M = _fd_case(seed, **kw)
+        fw = o.step_forward(W, X, lg, tau, L, N, M, loss="cosine")
+        g = o.step_backward(fw, X, W)["dlogits"]
+        mask = fw["mask"]
+        h = 1e-6
+        fd = np.zeros_like(lg)
+        for idx in np.ndindex(lg.shape):
+            lp = lg.copy(); lp[idx] += h
+            lm = lg.copy(); lm[idx] -= h
+            ep = o.step_forward(W, X, lp, tau, L, N, M, mask=mask, loss="cosine")["L"]
+            em = o.step_forward(W, X, lm, tau, L, N, M, mask=mask, loss="cosine")["L"]
+            fd[idx] = (ep - em) / (2 * h)
+        err = np.linalg.norm(g - fd) / np.linalg.norm(fd)
+        assert err < 1e-6, (seed, err)
+
+
+def pin_cosine_grad_geometry(o):
+    """Scale invariance of the cosine makes its gradient orthogonal to y~,
+    and by Cauchy-Schwarz it never points along y: <dL/dy~, y~> = 0 and
+    <dL/dy~, y> <= 0."""
+    W, X, lg, tau, L, N, M = _fd_case(32)
+    fw = o.step_forward(W, X, lg, tau, L, N, M, loss="cosine")
+    d = o.step_backward(fw, X, W)["dYt"]
+    Yt, Y = fw["Y_tilde"], fw["Y"]
+    assert abs(np.sum(d * Yt)) <= 1e-12 * np.linalg.norm(d) * np.linalg.norm(Yt)
+    assert np.sum(d * Y) < 0
+
+
+def _surrogate_loss(o, W, X, S, P, P0, M0, tau, L, N, M, loss):
+    """Objective with the mask replaced by M0 + S_hat(P) - S_hat(P0): equal to
+    the real objective at P0, with the identity as d mask / d S_hat."""
+    mask = M0 + o.block_permute(S, P) - o.block_permute(S, P0)
+    return o.step_forward(W, X, None, tau, L, N, M, P=P, mask=mask, loss=loss)["L"]
+
+
+def pin_mask_ste_fd(o):
+    """Straight-through gradient of the mask (soft P): step_backward with
+    mask_ste equals central differences of the surrogate objective whose mask
+    moves one for one with the permuted scores, for both objectives."""
+    for seed, loss in ((33, "frobenius"), (34, "cosine")):
+        W, X, lg, tau, L, N, M = _fd_case(seed, cout=5, cin=8, T=7, B=4, L=3)
+        fw = o.step_forward(W, X, lg, tau, L, N, M, loss=loss)
+        g = o.step_backward(fw, X, W, mask_ste=True)["dlogits"]
+        g0 = o.step_backward(fw, X, W)["dlogits"]
+        S, P0, M0 = fw["S"], fw["P"], fw["mask"].astype(np.float64)
+        h = 1e-6
+        fd = np.zeros_like(lg)
+        for idx in np.ndindex(lg.shape):
+            lp = lg.copy(); lp[idx] += h
+            lm = lg.copy(); lm[idx] -= h
+            ep = _surrogate_loss(o, W, X, S, o.sinkhorn(lp, tau, L), P0, M0, tau, L, N, M, loss)
+            em = _surrogate_loss(o, W, X, S, o.sinkhorn(lm, tau, L), P0, M0, tau, L, N, M, loss)
+            fd[idx] = (ep - em) / (2 * h)
+        err = np.linalg.norm(g - fd) / np.linalg.norm(fd)
+        assert err < 1e-6, (seed, loss, err)
+        assert np.linalg.norm(g - g0) > 1e-2 * np.linalg.norm(g0), (seed, loss)
+
+
+def pin_mask_ste_hard_dP_fd(o):
+    """Hardened step with the mask's straight-through term: d L / d P at the
+    hard P (block adjoint plus mask term) equals central differences in P of
+    the surrogate objective, for both objectives."""
+    rng = _rng(35)
+    cout, cin, T, B, tau, L = 5, 8, 7, 4, 0.8, 3
+    W = rng.standard_normal((cout, cin))
+    X = rng.standard_normal((T, cin))
+    lg = rng.standard_normal((cin // B, B, B))
+    for loss in ("frobenius", "cosine"):
+        fw = o.step_forward(W, X, lg, tau, L, 2, 4, hard=True, loss=loss)
+        dP = o.step_backward(fw, X, W, mask_ste=True)["dP"]
+        S, P0, M0 = fw["S"], fw["P"], fw["mask"].astype(np.float64)
+        h = 1e-6
+        fd = np.zeros_like(P0)
+        for idx in np.ndindex(P0.shape):
+            pp = P0.copy(); pp[idx] += h
+            pm = P0.copy(); pm[idx] -= h
+            fd[idx] = (_surrogate_loss(o, W, X, S, pp, P0, M0, tau, L, 2, 4, loss)
+                       - _surrogate_loss(o, W, X, S, pm, P0, M0, tau, L, 2, 4, loss)) / (2 * h)
+        err = np.linalg.norm(dP - fd) / np.linalg.norm(fd)
+        assert err < 1e-7, (loss, err)
+
+
+def pin_training_cosine(o):
+    """Training on the cosine objective (hardened forward, straight-through
+    backward through P and the mask) on the outlier-scaled layer: the learned
+    hard permutation has a lower cosine loss than plain Wanda (identity
+    permutation)."""
+    rng = _rng(27)
+    cout, cin, T, B = 16, 32, 24, 8
+    W = rng.standard_normal((cout, cin)) * 0.02
+    X = rng.standard_normal((T, cin)) * np.exp(rng.standard_normal(cin))[None, :]
+    nb = cin // B
+    lg0 = 3.0 * np.eye(B)[None].repeat(nb, axis=0) + 1e-3 * rng.standard_normal((nb, B, B))
+    eye = np.eye(B)[None].repeat(nb, axis=0)
+    wanda = o.step_forward(W, X, None, 1.0, 5, 2, 4, P=eye, loss="cosine")["L"]
+    lg, errs = o.train(W, X, lg0, 60, 5e-2, 2, 4, 5, hard=True, loss="cosine", mask_ste=True)
+    final = o.step_forward(W, X, lg, 0.1, 5, 2, 4, hard=True, loss="cosine")["L"]
+    assert abs(errs[0] - wanda) < 1e-12, (errs[0], wanda)
+    assert final < wanda, (final, wanda)
+
+
 ALL_PINS = [
     pin_sinkhorn_2x2_golden, pin_sinkhorn_uniform, pin_sinkhorn_closed_form,
     pin_sinkhorn_closed_form_values, pin_sinkhorn_doubly_stochastic,
@@ -594,5 +738,7 @@ ALL_PINS = [
     pin_cin8_enumeration, pin_step_gradient_fd, pin_block_adjoint_fd,
     pin_zero_error_gradient, pin_colnorm, pin_harden_bruteforce,
     pin_hard_forward_planted, pin_straight_through_gradient_fd, pin_adamw_torch,
-    pin_tau_schedule, pin_training_beats_wanda,
+    pin_tau_schedule, pin_training_beats_wanda, pin_cosine_closed_forms,
+    pin_cosine_dense_is_zero, pin_cosine_gradient_fd, pin_cosine_grad_geometry,
+    pin_mask_ste_fd, pin_mask_ste_hard_dP_fd, pin_training_cosine,
 ]

@@ -142,10 +142,10 @@ def _adjoint_forward_order(dP, P, trace, tau):
     return G / tau
 
 
-def _backward_unscaled(fw, X, W):
+def _backward_unscaled(fw, X, W, mask_ste=False):
     fw2 = dict(fw)
     fw2["E"] = 1.0
-    return _orig["step_backward"](fw2, X, W)
+    return _orig["step_backward"](fw2, X, W, mask_ste)
 
 
 def _harden_minimise(P):
@@ -156,16 +156,16 @@ def _harden_transposed(P):
     return np.transpose(_orig["harden"](P), (0, 2, 1))
 
 
-def _ste_hard_in_sinkhorn_adjoint(fw, X, W):
+def _ste_hard_in_sinkhorn_adjoint(fw, X, W, mask_ste=False):
     fw2 = dict(fw)
     fw2["P_soft"] = fw["P"]
-    return _orig["step_backward"](fw2, X, W)
+    return _orig["step_backward"](fw2, X, W, mask_ste)
 
 
-def _ste_soft_in_block_adjoint(fw, X, W):
+def _ste_soft_in_block_adjoint(fw, X, W, mask_ste=False):
     fw2 = dict(fw)
     fw2["P"] = fw["P_soft"]
-    return _orig["step_backward"](fw2, X, W)
+    return _orig["step_backward"](fw2, X, W, mask_ste)
 
 
 def _adamw_no_bias_correction(param, grad, m, v, t, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
@@ -186,6 +186,72 @@ def _tau_reversed(t, steps, tau0=1.0, tau1=0.1):
 
 def _train_soft(W, X, logits, steps, lr, N, M, iters, hard=True, **kw):
     return _orig["train"](W, X, logits, steps, lr, N, M, iters, hard=False, **kw)
+
+
+def _cosine_norm_y_squared(Y, Yt):
+    y = np.asarray(Y, dtype=np.float64).ravel()
+    yt = np.asarray(Yt, dtype=np.float64).ravel()
+    return float(1.0 - np.dot(y, yt) / np.dot(y, y))
+
+
+def _cosine_similarity_not_loss(Y, Yt):
+    return 1.0 - _orig["cosine_loss"](Y, Yt)
+
+
+def _cosine_grad_cube_dropped(Y, Yt):
+    Y = np.asarray(Y, dtype=np.float64)
+    Yt = np.asarray(Yt, dtype=np.float64)
+    ny, nt = np.linalg.norm(Y), np.linalg.norm(Yt)
+    return -Y / (ny * nt) + np.sum(Y * Yt) * Yt / (ny * nt ** 2)
+
+
+def _cosine_grad_first_term(Y, Yt):
+    Y = np.asarray(Y, dtype=np.float64)
+    return -Y / (np.linalg.norm(Y) * np.linalg.norm(np.asarray(Yt, dtype=np.float64)))
+
+
+def _cosine_of_residual(W, X, logits, tau, iters, N, M, P=None, mask=None, hard=False,
+                        loss="frobenius"):
+    fw = _orig["step_forward"](W, X, logits, tau, iters, N, M, P, mask, hard, loss)
+    if loss == "cosine":
+        fw["L"] = olcp.cosine_loss(fw["Y"], fw["R"])
+    return fw
+
+
+def _ste_without_weight(G, W, S, P):
+    return _orig["mask_ste_adjoint"](G, np.ones_like(np.asarray(W, dtype=np.float64)), S, P)
+
+
+def _ste_unscaled_importance(G, W, S, P):
+    return _orig["mask_ste_adjoint"](G, W, np.abs(np.asarray(W, dtype=np.float64)), P)
+
+
+def _ste_sign(G, W, S, P):
+    return -_orig["mask_ste_adjoint"](G, W, S, P)
+
+
+def _ste_unpermuted_weight(G, W, S, P):
+    P = np.asarray(P, dtype=np.float64)
+    nb, B, _ = P.shape
+    rows = G.shape[0]
+    Gb = np.asarray(G, dtype=np.float64).reshape(rows, nb, B).transpose(1, 0, 2)
+    Wb = np.asarray(W, dtype=np.float64).reshape(rows, nb, B).transpose(1, 0, 2)
+    Sb = np.asarray(S, dtype=np.float64).reshape(rows, nb, B).transpose(1, 0, 2)
+    return np.matmul(Sb.transpose(0, 2, 1), np.matmul(Gb, P) * Wb)
+
+
+def _ste_mask_term_at_soft_P(fw, X, W, mask_ste=False):
+    out = _orig["step_backward"](fw, X, W)
+    if mask_ste:
+        dP = out["dP"] + olcp.mask_ste_adjoint(out["G"], W, fw["S"], fw["P_soft"])
+        out["dP"] = dP
+        out["dlogits"] = olcp.sinkhorn_adjoint(dP, fw["P_soft"], fw["trace"], fw["tau"])
+    return out
+
+
+def _train_ignores_loss(W, X, logits, steps, lr, N, M, iters, hard=True, loss="frobenius",
+                        mask_ste=False, **kw):
+    return _orig["train"](W, X, logits, steps, lr, N, M, iters, hard=hard, mask_ste=mask_ste, **kw)
 
 
 MUTATIONS = [
@@ -221,6 +287,17 @@ MUTATIONS = [
     ("adamw", _adamw_coupled_decay),
     ("tau_schedule", _tau_reversed),
     ("train", _train_soft),
+    ("cosine_loss", _cosine_norm_y_squared),
+    ("cosine_loss", _cosine_similarity_not_loss),
+    ("cosine_grad", _cosine_grad_cube_dropped),
+    ("cosine_grad", _cosine_grad_first_term),
+    ("step_forward", _cosine_of_residual),
+    ("mask_ste_adjoint", _ste_without_weight),
+    ("mask_ste_adjoint", _ste_unscaled_importance),
+    ("mask_ste_adjoint", _ste_sign),
+    ("mask_ste_adjoint", _ste_unpermuted_weight),
+    ("step_backward", _ste_mask_term_at_soft_P),
+    ("train", _train_ignores_loss),
 ]
 
 # the full 8! enumeration is covered by the plain pin run; the rest are fast
