@@ -46,6 +46,11 @@ def parse():
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
     ap.add_argument("--harden", action="store_true",
                     help="hardened forward + straight-through backward (another workload)")
+    ap.add_argument("--cosine", action="store_true",
+                    help="cosine objective of the layer outputs (another workload; the dense outputs are "
+                         "part of the per-layer setup of every step)")
+    ap.add_argument("--mask-ste", action="store_true",
+                    help="straight-through gradient of the mask in the backward (another workload)")
     ap.add_argument("--adamw", action="store_true",
                     help="training step: the backward with the fused AdamW update of the logits")
     ap.add_argument("--saturate", action="store_true",
@@ -126,7 +131,7 @@ class _Ev:
         self.cuda_event = h.value
 
 
-def cpu_baseline(spec, lay, hard=False):
+def cpu_baseline(spec, lay, hard=False, loss="frobenius", mask_ste=False):
     """The float64 oracle, untuned, for one full forward + backward step of the
     same layer on the host cores (one step is the sample)."""
     import oracle
@@ -136,9 +141,10 @@ def cpu_baseline(spec, lay, hard=False):
     except Exception:  # noqa: BLE001
         cores = os.cpu_count()
     t0 = time.perf_counter()
-    fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M, hard=hard)
+    fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M, hard=hard,
+                             loss=loss)
     if spec.backward:
-        oracle.step_backward(fw, lay.X, lay.W)
+        oracle.step_backward(fw, lay.X, lay.W, mask_ste=mask_ste)
     dt = time.perf_counter() - t0
     return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
             "sample": "one full %s step of the same %dx%d layer (T=%d), float64 NumPy, %.1f s"
@@ -212,7 +218,9 @@ def main():
     X = torch.from_numpy(lay.X).to(dev).to(tdt)
     logits = torch.from_numpy(lay.logits).to(dev)
     dlogits = torch.empty_like(logits)
-    sess = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, spec.N, spec.M, harden=args.harden)
+    loss = "cosine" if args.cosine else "frobenius"
+    sess = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, spec.N, spec.M, harden=args.harden, loss=loss,
+                            mask_ste=args.mask_ste)
     stream = torch.cuda.current_stream()
 
     m_state = torch.zeros_like(logits)
@@ -266,8 +274,10 @@ def main():
                            "ms": round(bwd_gemm_ms if dom_name == "error_gemm" else fwd_gemm_ms, 4)}}
 
     if args.breakdown:
-        fwd_names = FWD_NAMES + (["harden"] if args.harden else [])
-        names = fwd_names + (BWD_NAMES if spec.backward else [])
+        fwd_names = FWD_NAMES[:3] + (["cosine_finalize"] if args.cosine else FWD_NAMES[3:]) \
+            + (["harden"] if args.harden else [])
+        bwd_names = BWD_NAMES + (["cosine_grad"] if args.cosine else [])
+        names = fwd_names + (bwd_names if spec.backward else [])
         reps = 20
         evs = {n: [(he.new(), he.new()) for _ in range(reps)] for n in names}
         init_ev = [(ev(), ev()) for _ in range(reps)]
@@ -279,8 +289,8 @@ def main():
             tf = lcp.make_timing([_Ev(evs[n][r][0]) for n in fwd_names], [_Ev(evs[n][r][1]) for n in fwd_names])
             sess.forward(logits, timing=tf)
             if spec.backward:
-                tb = lcp.make_timing([_Ev(evs[n][r][0]) for n in BWD_NAMES],
-                                     [_Ev(evs[n][r][1]) for n in BWD_NAMES])
+                tb = lcp.make_timing([_Ev(evs[n][r][0]) for n in bwd_names],
+                                     [_Ev(evs[n][r][1]) for n in bwd_names])
                 sess.backward(logits, dlogits, timing=tb)
         torch.cuda.synchronize()
         print("per-kernel ms (mean of %d):" % reps, file=sys.stderr)
@@ -294,7 +304,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, lay, hard=args.harden)
+        cpu = cpu_baseline(spec, lay, hard=args.harden, loss=loss, mask_ste=args.mask_ste)
 
     out = {
         "metric": "LCP %s steps/sec per layer (%dx%d, %d:%d)" % ("fwd+bwd" if spec.backward else "fwd",
@@ -312,10 +322,12 @@ def main():
         "data": "synthetic (seeded LLaMA-shaped layer; no weights or calibration text available)",
         "config": {"workload": ("lcp_step_fwd_bwd" if spec.backward else "lcp_step_fwd")
                                + ("_hardened" if args.harden else "")
+                               + ("_cosine" if args.cosine else "")
+                               + ("_maskste" if (args.mask_ste and spec.backward) else "")
                                + ("_adamw" if (args.adamw and spec.backward) else ""),
                    "layer": spec.name, "cout": spec.cout, "cin": spec.cin,
                    "T": spec.T, "B": spec.B, "sinkhorn_iters": spec.iters, "tau": spec.tau,
-                   "N": spec.N, "M": spec.M, "backward": spec.backward,
+                   "N": spec.N, "M": spec.M, "backward": spec.backward, "objective": loss,
                    "includes_layer_setup": True},
         "roofline": roof,
         "cpu_baseline": cpu,

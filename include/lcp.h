@@ -12,6 +12,10 @@
  *   W_tilde = (W_hat . M) P_B^T,  D = W - W_tilde,  R = D X^T,  E = ||R||_F
  *   backward: dE/dL through the block permutation and the unrolled Sinkhorn,
  *   with the mask held constant.
+ * Options of the step (lcp_cfg): the hardened forward of [PermLLM] Method 2;
+ * the cosine objective of [PermLLM] (optimisation objective) in place of E;
+ * the straight-through gradient of the mask's argmax ([PermLLM] integration
+ * with pruning methods).
  *
  * Conventions shared by every entry point:
  *   - Matrices are row-major. W is Cout x Cin (like a linear layer), X is
@@ -66,10 +70,23 @@ typedef struct lcp_layer {
                           lcp_layer_init (X transposed, zero beyond T); used
                           by the backward. May be NULL for F32 layers.        */
   const float* norms;  /* [cin] ||X[:, j]||_2, written by lcp_layer_init      */
+  const void*  Y;      /* cosine objective only (else may be NULL): the dense
+                          outputs W X^T, [cout][lcp_xt_pitch(T)] dtype, zero
+                          beyond column T, written by lcp_layer_outputs      */
+  const float* y2;     /* cosine objective only: 1 fp32, ||Y||_F^2, written by
+                          lcp_layer_outputs                                   */
   lcp_dtype    dtype;
   int          cout, cin, T;
   int          B;      /* block size, 32, 64 or 128; cin % B == 0            */
 } lcp_layer;
+
+/* Objectives (lcp_cfg.loss). */
+#define LCP_LOSS_FROBENIUS 0  /* E = ||(W - W_tilde) X^T||_F                  */
+#define LCP_LOSS_COSINE    1  /* [PermLLM] optimisation objective
+                                 1 - y.y~ / (||y|| ||y~||) with y = vec(W X^T),
+                                 y~ = vec(W_tilde X^T): one cosine over the
+                                 layer's whole output; 1 (gradient 0) when
+                                 either norm is 0                            */
 
 /* Hyper-parameters of one step. */
 typedef struct lcp_cfg {
@@ -80,13 +97,22 @@ typedef struct lcp_cfg {
                    hardened P of lcp_harden ([PermLLM] Method 2) and the
                    backward is straight-through: dE/dP at the hard P is handed
                    unchanged to the adjoint of the soft Sinkhorn.              */
+  int   loss;   /* LCP_LOSS_FROBENIUS or LCP_LOSS_COSINE (needs L->Y, L->y2)  */
+  int   mask_ste; /* 0: the mask is constant in the backward. 1: the gradient
+                   reaching the 0/1 mask, (G_b P_b) . W_hat_b with
+                   G = dL/dW_tilde, is handed unchanged to the permuted scores
+                   S_hat_b = S_b P_b (straight-through estimator for the
+                   argmax), adding S_b^T ((G_b P_b) . (W_b P_b)) to dL/dP_b;
+                   S = |W| . norms. Under harden every P here is the hard P. */
 } lcp_cfg;
 
 /* Optional per-kernel timing hooks: hipEvent_t handles (as void*) recorded on
  * the step's stream immediately before (start[i]) and after (stop[i]) kernel i
  * of the step. NULL entries are skipped; a NULL lcp_timing* records nothing.
  * Forward kernels: 0 Sinkhorn, 1 permute+mask+unpermute, 2 error GEMM,
- * 3 error finalisation, 4 hardening (harden = 1 only). Backward kernels: 0 dD GEMM, 1 block adjoint, 2 Sinkhorn adjoint. */
+ * 3 error (or cosine) finalisation, 4 hardening (harden = 1 only). Backward
+ * kernels: 0 dD GEMM, 1 block adjoint, 2 Sinkhorn adjoint, 3 cosine
+ * gradient dL/dY~ (cosine objective only). */
 typedef struct lcp_timing {
   void* start[8];
   void* stop[8];
@@ -193,6 +219,17 @@ int lcp_error(const void* W, const void* Wt, const void* X, lcp_dtype dt,
               int cout, int cin, int T, float* err, void* R_out, void* ws,
               size_t ws_bytes, void* stream);
 
+/* lcp_layer_outputs - per-layer constants of the cosine objective ([PermLLM]
+ * optimisation objective compares the dense outputs y with the sparse ones):
+ *   Y = W X^T, [cout][lcp_xt_pitch(T)] in dt (columns T .. pitch-1 written 0);
+ *   *y2 = ||Y||_F^2 (fp32, device), summed over the fp32 accumulators.
+ * BF16 multiplies with bf16 MFMA and fp32 accumulation and rounds Y to bf16.
+ *   W: [cout][cin] dt; X: [T][cin] dt; all 16-byte aligned; cin % 32 == 0.
+ *   ws: lcp_error_workspace_bytes(cout, cin, T, dt) bytes (256-aligned). */
+int lcp_layer_outputs(const void* W, const void* X, lcp_dtype dt, int cout,
+                      int cin, int T, void* Y, float* y2, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Full step. The workspace carries the forward's saved state (P, Sinkhorn
  * offsets, mask bits, residual R, E) to the backward; it must not be touched
@@ -203,7 +240,8 @@ int lcp_step_workspace_bytes(int cout, int cin, int T, int B, int iters,
                              lcp_dtype dt, size_t* bytes);
 
 /* lcp_step_fwd - Sinkhorn, (hardening,) permute, importance, N:M mask,
- * un-permute, difference, error GEMM: *err = E. Optional copies: P_out
+ * un-permute, difference, error GEMM: *err = the objective of c->loss (E, or
+ * the cosine loss). Optional copies: P_out
  * [nb][B][B] fp32 (the P the forward used: P_hat, or the hard P when
  * c->harden), bits_out [cout][cin/32] uint32 (the mask in permuted
  * positions). */
@@ -211,9 +249,10 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c,
                  void* ws, size_t ws_bytes, float* err, float* P_out,
                  uint32_t* bits_out, const lcp_timing* tm, void* stream);
 
-/* lcp_step_bwd - dlogits = dE/dlogits ([nb][B][B] fp32) with the mask of the
- * matching lcp_step_fwd held constant; zero when E == 0. Needs L->Xt for BF16
- * layers. */
+/* lcp_step_bwd - dlogits = dL/dlogits ([nb][B][B] fp32) of the objective L of
+ * c->loss, with the mask of the matching lcp_step_fwd held constant unless
+ * c->mask_ste; zero when E == 0 (Frobenius) or when ||Y|| ||Y~|| == 0
+ * (cosine). c must equal the forward's. Needs L->Xt for BF16 layers. */
 int lcp_step_bwd(const lcp_layer* L, const float* logits, const lcp_cfg* c,
                  void* ws, size_t ws_bytes, float* dlogits,
                  const lcp_timing* tm, void* stream);
@@ -251,8 +290,9 @@ int lcp_step_bwd_adamw(const lcp_layer* L, float* logits, const lcp_cfg* c,
 
 /* lcp_train - `steps` optimisation steps of one layer's logits in place:
  * for t = 0 .. steps-1, tau_t = tau0 + (tau1 - tau0) t / (steps - 1), then
- * lcp_step_fwd (E written to errs[t], device fp32) and lcp_step_bwd_adamw
- * with AdamW step t + 1. c->iters, N, M, harden apply to every step (the
+ * lcp_step_fwd (its objective written to errs[t], device fp32) and
+ * lcp_step_bwd_adamw with AdamW step t + 1. c->iters, N, M, harden, loss and
+ * mask_ste apply to every step (the
  * pages train with the hardened forward); c->tau is ignored. m, v: AdamW
  * state as for lcp_step_bwd_adamw. Arguments are validated before the first
  * step; a launch error stops the loop and is returned. */

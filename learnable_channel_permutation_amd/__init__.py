@@ -14,7 +14,7 @@ from ._lib import (LCP_BF16, LCP_F32, LcpError, lcp_colnorm, lcp_error,  # noqa:
                    lcp_error_workspace_bytes, lcp_harden, lcp_layer_init, lcp_nm_mask, lcp_permute,
                    lcp_sinkhorn, lcp_sinkhorn_bwd, lcp_step_bwd, lcp_step_fwd,
                    lcp_step_workspace_bytes, lcp_xt_pitch, make_cfg, make_layer, make_timing,
-                   lcp_adamw, lcp_step_bwd_adamw, lcp_train, make_adamw_cfg)
+                   lcp_adamw, lcp_step_bwd_adamw, lcp_train, make_adamw_cfg, lcp_layer_outputs)
 
 __all__ = ["LayerSession", "LcpError"] + [n for n in _lib.EXPORTS if n.startswith("lcp_")]
 
@@ -25,10 +25,14 @@ class LayerSession:
     Holds W and X (caller tensors on one GPU), the per-layer setup written by
     lcp_layer_init (column norms; X transposed for bf16 layers) and one step
     workspace sized by lcp_step_workspace_bytes. harden=True runs the
-    hardened forward with the straight-through backward.
+    hardened forward with the straight-through backward; loss="cosine"
+    optimises the cosine objective (the dense outputs Y = W X^T and ||Y||^2
+    are then computed once here by lcp_layer_outputs); mask_ste=True adds the
+    straight-through gradient of the mask.
     """
 
-    def __init__(self, W, X, B, iters, tau, N, M, stream=None, harden=False):
+    def __init__(self, W, X, B, iters, tau, N, M, stream=None, harden=False, loss="frobenius",
+                 mask_ste=False):
         if W.device != X.device or W.dtype != X.dtype:
             raise ValueError("W and X must share device and dtype")
         self.W, self.X = W, X
@@ -43,13 +47,24 @@ class LayerSession:
         nbytes = lcp_step_workspace_bytes(cout, cin, T, B, iters, _lib.dtype_code(W))
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.err = torch.empty(1, dtype=torch.float32, device=dev)
-        self.layer = make_layer(W, X, self.norms, B, self.Xt)
-        self.cfg = make_cfg(iters, tau, N, M, harden)
+        self.Y = self.y2 = None
+        if loss == "cosine":
+            self.Y = torch.empty((cout, lcp_xt_pitch(T)), dtype=W.dtype, device=dev)
+            self.y2 = torch.empty(1, dtype=torch.float32, device=dev)
+        self.layer = make_layer(W, X, self.norms, B, self.Xt, self.Y, self.y2)
+        self.cfg = make_cfg(iters, tau, N, M, harden, loss, mask_ste)
         self.init(stream)
 
     def init(self, stream=None):
-        """Per-layer setup (column norms, transposed X)."""
+        """Per-layer setup (column norms, transposed X; dense outputs and
+        their squared norm for the cosine objective)."""
         lcp_layer_init(self.X, self.norms, self.Xt, stream=stream)
+        if self.Y is not None:
+            cout, cin = self.W.shape
+            ebytes = lcp_error_workspace_bytes(cout, cin, self.X.shape[0], _lib.dtype_code(self.W))
+            if ebytes > self.ws.numel():
+                raise RuntimeError("step workspace smaller than the layer-output workspace")
+            lcp_layer_outputs(self.W, self.X, self.Y, self.y2, self.ws, stream=stream)
 
     def forward(self, logits, P_out=None, bits_out=None, timing=None, stream=None):
         lcp_step_fwd(self.layer, logits, self.cfg, self.ws, self.err, P_out, bits_out, timing, stream)
@@ -65,7 +80,7 @@ class LayerSession:
               weight_decay=0.01, stream=None):
         """`steps` AdamW steps on `logits` (updated in place) with the
         temperature annealed linearly from tau0 to tau1 (lcp_train). Returns
-        the per-step errors E as a device tensor."""
+        the per-step objective values as a device tensor."""
         m = torch.zeros_like(logits)
         v = torch.zeros_like(logits)
         errs = torch.empty(steps, dtype=torch.float32, device=logits.device)

@@ -24,23 +24,29 @@ LCP_E_HIP = -4
 LCP_F32 = 0
 LCP_BF16 = 1
 
+LCP_LOSS_FROBENIUS = 0
+LCP_LOSS_COSINE = 1
+
 EXPORTS = [
     "lcp_status_string", "lcp_version", "lcp_sinkhorn", "lcp_sinkhorn_bwd", "lcp_colnorm",
     "lcp_xt_pitch", "lcp_layer_init", "lcp_permute", "lcp_nm_mask",
     "lcp_error_workspace_bytes", "lcp_error", "lcp_step_workspace_bytes", "lcp_step_fwd",
     "lcp_step_bwd", "lcp_harden", "lcp_adamw", "lcp_step_bwd_adamw", "lcp_train",
+    "lcp_layer_outputs",
 ]
 
 
 class lcp_layer(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("X", ctypes.c_void_p), ("Xt", ctypes.c_void_p),
-                ("norms", ctypes.c_void_p), ("dtype", ctypes.c_int), ("cout", ctypes.c_int),
-                ("cin", ctypes.c_int), ("T", ctypes.c_int), ("B", ctypes.c_int)]
+                ("norms", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("y2", ctypes.c_void_p),
+                ("dtype", ctypes.c_int), ("cout", ctypes.c_int), ("cin", ctypes.c_int),
+                ("T", ctypes.c_int), ("B", ctypes.c_int)]
 
 
 class lcp_cfg(ctypes.Structure):
     _fields_ = [("iters", ctypes.c_int), ("tau", ctypes.c_float), ("N", ctypes.c_int),
-                ("M", ctypes.c_int), ("harden", ctypes.c_int)]
+                ("M", ctypes.c_int), ("harden", ctypes.c_int), ("loss", ctypes.c_int),
+                ("mask_ste", ctypes.c_int)]
 
 
 class lcp_adamw_cfg(ctypes.Structure):
@@ -83,6 +89,7 @@ def _load():
         "lcp_nm_mask": (i, [vp, i, i, i, i, vp, vp]),
         "lcp_error_workspace_bytes": (i, [i, i, i, i, psz]),
         "lcp_error": (i, [vp, vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
+        "lcp_layer_outputs": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
         "lcp_step_workspace_bytes": (i, [i, i, i, i, i, i, psz]),
         "lcp_step_fwd": (i, [ctypes.POINTER(lcp_layer), vp, ctypes.POINTER(lcp_cfg), vp, sz, vp, vp, vp,
                              ctypes.POINTER(lcp_timing), vp]),
@@ -194,6 +201,14 @@ def lcp_error(W, Wt, X, err, ws, R_out=None, stream=None):
                                              _stream(stream)))
 
 
+def lcp_layer_outputs(W, X, Y, y2, ws, stream=None):
+    cout, cin = W.shape
+    T = X.shape[0]
+    return _check("lcp_layer_outputs",
+                  LIB.lcp_layer_outputs(_p(W), _p(X), dtype_code(W), cout, cin, T, _p(Y), _p(y2), _p(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def lcp_step_workspace_bytes(cout, cin, T, B, iters, dtype):
     out = ctypes.c_size_t(0)
     _check("lcp_step_workspace_bytes",
@@ -201,14 +216,17 @@ def lcp_step_workspace_bytes(cout, cin, T, B, iters, dtype):
     return out.value
 
 
-def make_layer(W, X, norms, B, Xt=None):
+def make_layer(W, X, norms, B, Xt=None, Y=None, y2=None):
     cout, cin = W.shape
     return lcp_layer(W.data_ptr(), X.data_ptr(), None if Xt is None else Xt.data_ptr(), norms.data_ptr(),
+                     None if Y is None else Y.data_ptr(), None if y2 is None else y2.data_ptr(),
                      dtype_code(W), cout, cin, X.shape[0], B)
 
 
-def make_cfg(iters, tau, N, M, harden=False):
-    return lcp_cfg(int(iters), float(tau), int(N), int(M), 1 if harden else 0)
+def make_cfg(iters, tau, N, M, harden=False, loss="frobenius", mask_ste=False):
+    codes = {"frobenius": LCP_LOSS_FROBENIUS, "cosine": LCP_LOSS_COSINE}
+    return lcp_cfg(int(iters), float(tau), int(N), int(M), 1 if harden else 0, codes[loss],
+                   1 if mask_ste else 0)
 
 
 def make_timing(starts=(), stops=()):

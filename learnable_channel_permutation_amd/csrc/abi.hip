@@ -25,7 +25,7 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int pitch_of(int T) { return (T + 63) / 64 * 64; }
 
 struct StepLayout {
-  size_t P, Ph, off, bits, D, R, part, E, adj, fragF, fragA, total;
+  size_t P, Ph, off, bits, D, R, part, party, E, GY, adj, fragF, fragA, total;
   int nb, pitch, nparts;
   AdjSplit sp;
 };
@@ -45,7 +45,9 @@ StepLayout step_layout(int cout, int cin, int T, int B, int iters, lcp_dtype dt)
   L.D = o;     o += align_up((size_t)cout * cin * esize(dt));
   L.R = o;     o += align_up((size_t)cout * L.pitch * esize(dt));
   L.part = o;  o += align_up((size_t)L.nparts * 4);
-  L.E = o;     o += align_up(4);
+  L.party = o; o += align_up((size_t)L.nparts * 4);
+  L.E = o;     o += align_up(4 * 4);    // E, dD factor, cosine coefficients of Y and R
+  L.GY = o;    o += align_up((size_t)cout * L.pitch * esize(dt));   // cosine dL/dY~
   L.adj = o;   o += align_up((size_t)L.sp.grid * L.sp.maxseg * B * B * 4);
   L.fragF = o; o += bf ? align_up((size_t)L.nb * frag_fwd_entries(B) * 16) : 0;
   L.fragA = o; o += bf ? align_up((size_t)L.nb * frag_adj_entries(B) * 16) : 0;
@@ -61,6 +63,9 @@ int check_step_args(const lcp_layer* L, const float* logits, const lcp_cfg* c) {
   if (c->iters < 1 || !good_tau(c->tau)) return LCP_E_INVAL;
   if (c->M <= 0 || c->N < 1 || c->N >= c->M) return LCP_E_INVAL;
   if (c->harden != 0 && c->harden != 1) return LCP_E_INVAL;
+  if (c->mask_ste != 0 && c->mask_ste != 1) return LCP_E_INVAL;
+  if (c->loss != LCP_LOSS_FROBENIUS && c->loss != LCP_LOSS_COSINE) return LCP_E_INVAL;
+  if (c->loss == LCP_LOSS_COSINE && (!L->Y || !L->y2 || !aligned16(L->Y))) return LCP_E_INVAL;
   if (L->cin % L->B != 0 || L->B % c->M != 0) return LCP_E_INVAL;
   if (!good_B(L->B)) return LCP_E_UNSUPPORTED;
   if (c->M != 4 && c->M != 8) return LCP_E_UNSUPPORTED;
@@ -130,6 +135,16 @@ static int step_bwd_impl(const lcp_layer* L, const float* logits, const lcp_cfg*
   hipStream_t s = S(stream);
   const Timer tmr{tm, s};
 
+  if (c->loss == LCP_LOSS_COSINE) {
+    // dL/dY~ from Y and R with the forward's coefficients; the dD GEMM then
+    // forms G = dL/dW_tilde = (dL/dY~) X (factor 1)
+    void* GY = base + Ly.GY;
+    tmr.start(3);
+    LCP_RUN(launch_cosine_grad(L->Y, R, (size_t)L->cout * Ly.pitch, bf, Ews, GY, s));
+    tmr.stop(3);
+    R = GY;
+  }
+  const float* ste = c->mask_ste ? L->norms : nullptr;
   tmr.start(0);
   if (bf)
     LCP_RUN(launch_gemm_dd_bf16((const uint16_t*)R, Ly.pitch, (const uint16_t*)L->Xt, Ly.pitch, L->cout, L->cin,
@@ -142,10 +157,10 @@ static int step_bwd_impl(const lcp_layer* L, const float* logits, const lcp_cfg*
   tmr.start(1);
   if (bf)
     LCP_RUN(launch_adjoint_bf16((const uint16_t*)Gd, (const uint16_t*)L->W, fragA, P, bits, L->cout, L->cin,
-                                L->B, Ly.sp, adj, s));
+                                L->B, Ly.sp, ste, adj, s));
   else
     LCP_RUN(launch_adjoint_f32((const float*)Gd, (const float*)L->W, P, bits, L->cout, L->cin, L->B, Ly.sp,
-                               adj, s));
+                               ste, adj, s));
   tmr.stop(1);
   tmr.start(2);
   LCP_RUN(launch_sinkhorn_bwd(logits, adj, &Ly.sp, off, dlogits, Ly.nb, L->B, c->iters, c->tau, opt, s));
@@ -289,11 +304,36 @@ int lcp_error(const void* W, const void* Wt, const void* X, lcp_dtype dt, int co
   LCP_RUN(launch_diff(W, Wt, cout * cin, dt == LCP_BF16, D, s));
   if (dt == LCP_BF16)
     LCP_RUN(launch_gemm_error_bf16((const uint16_t*)D, cin, (const uint16_t*)X, cin, cout, T, pitch, cin,
-                                   (uint16_t*)R, pitch, part, s));
+                                   (uint16_t*)R, pitch, part, nullptr, nullptr, s));
   else
     LCP_RUN(launch_gemm_error_f32((const float*)D, cin, (const float*)X, cin, cout, T, pitch, cin, (float*)R,
-                                  pitch, part, s));
+                                  pitch, part, nullptr, nullptr, s));
   LCP_RUN(launch_error_finalize(part, nparts, Ews, err, s));
+  return LCP_OK;
+}
+
+int lcp_layer_outputs(const void* W, const void* X, lcp_dtype dt, int cout, int cin, int T, void* Y, float* y2,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !X || !Y || !y2 || cout <= 0 || cin <= 0 || T <= 0) return LCP_E_INVAL;
+  if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
+  if (cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LCP_E_INVAL;
+  size_t need = 0;
+  int rc = lcp_error_workspace_bytes(cout, cin, T, dt, &need);
+  if (rc != LCP_OK) return rc;
+  rc = check_ws(ws, ws_bytes, need);
+  if (rc != LCP_OK) return rc;
+  const int pitch = pitch_of(T);
+  const int nparts = gemm_error_parts(cout, pitch, dt == LCP_BF16);
+  float* part = (float*)ws;
+  hipStream_t s = S(stream);
+  if (dt == LCP_BF16)
+    LCP_RUN(launch_gemm_error_bf16((const uint16_t*)W, cin, (const uint16_t*)X, cin, cout, T, pitch, cin,
+                                   (uint16_t*)Y, pitch, part, nullptr, nullptr, s));
+  else
+    LCP_RUN(launch_gemm_error_f32((const float*)W, cin, (const float*)X, cin, cout, T, pitch, cin, (float*)Y,
+                                  pitch, part, nullptr, nullptr, s));
+  LCP_RUN(launch_sum_finalize(part, nparts, y2, s));
   return LCP_OK;
 }
 
@@ -323,10 +363,12 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
   void* D = base + Ly.D;
   void* R = base + Ly.R;
   float* part = (float*)(base + Ly.part);
+  float* party = (float*)(base + Ly.party);
   float* Ews = (float*)(base + Ly.E);
   hipStream_t s = S(stream);
   const Timer tmr{tm, s};
   const bool bf = L->dtype == LCP_BF16;
+  const bool cosine = c->loss == LCP_LOSS_COSINE;
 
   u32x4* fragF = (u32x4*)(base + Ly.fragF);
   u32x4* fragA = (u32x4*)(base + Ly.fragA);
@@ -352,16 +394,20 @@ int lcp_step_fwd(const lcp_layer* L, const float* logits, const lcp_cfg* c, void
     LCP_RUN(launch_permute_f32((const float*)L->W, L->cout, L->cin, L->norms, Pu, L->B, 0, PERM_FWD, (float*)D,
                                bits, c->N, c->M, s));
   tmr.stop(1);
+  // the cosine objective also needs <Y, R> (second partial set)
   tmr.start(2);
   if (bf)
     LCP_RUN(launch_gemm_error_bf16((const uint16_t*)D, L->cin, (const uint16_t*)L->X, L->cin, L->cout, L->T,
-                                   Ly.pitch, L->cin, (uint16_t*)R, Ly.pitch, part, s));
+                                   Ly.pitch, L->cin, (uint16_t*)R, Ly.pitch, part,
+                                   cosine ? (const uint16_t*)L->Y : nullptr, party, s));
   else
     LCP_RUN(launch_gemm_error_f32((const float*)D, L->cin, (const float*)L->X, L->cin, L->cout, L->T, Ly.pitch,
-                                  L->cin, (float*)R, Ly.pitch, part, s));
+                                  L->cin, (float*)R, Ly.pitch, part, cosine ? (const float*)L->Y : nullptr,
+                                  party, s));
   tmr.stop(2);
   tmr.start(3);
-  LCP_RUN(launch_error_finalize(part, Ly.nparts, Ews, err, s));
+  if (cosine) LCP_RUN(launch_cosine_finalize(part, party, Ly.nparts, L->y2, Ews, err, s));
+  else LCP_RUN(launch_error_finalize(part, Ly.nparts, Ews, err, s));
   tmr.stop(3);
   if (P_out)
     LCP_RUN(hipMemcpyAsync(P_out, Pu, (size_t)Ly.nb * L->B * L->B * 4, hipMemcpyDeviceToDevice, s));

@@ -22,6 +22,10 @@
 //      MFMA against the identity (exact: bf16 x 1.0 in fp32);
 //   4. dP^T[k][j] += sum_i A[i][k] G[i][j] + (Y . M)[i][k] W[i][j], MFMA with
 //      the rows i in the K slots on both sides.
+// With the straight-through mask term (STE) step 4 also adds
+//   dP^T[k][j] += sum_i (W_hat . Y)[i][k] S[i][j],  S[i][j] = |W[i][j]| n_j,
+// which is S_b^T ((G_b P_b) . (W_b P_b)): the gradient reaching the 0/1 mask,
+// dE/dM = (G_b P_b) . W_hat_b, handed unchanged to S_hat_b = S_b P_b.
 // For B = 128 the four waves of a workgroup take the same 32-row tile, share
 // one ring (each wave issues a quarter of the loads, a barrier per tile) and
 // each owns one 32-wide column block of dP (register budget); for B <= 64
@@ -66,11 +70,11 @@ __device__ __forceinline__ u32x4 identity_slots(int v, int h, int n) {
 // of the block-major sequence of 32-row tiles (tpb tiles per block), which
 // spans at most `maxseg` blocks; it writes one partial B x B matrix per block
 // segment to part[(g * maxseg + k) * B * B] (k = block - first block of g).
-template <int B>
+template <int B, bool STE>
 __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ W, const u32x4* __restrict__ gfrag,
     const float* __restrict__ P, const uint32_t* __restrict__ bits, int cout, int cin, int tpw,
-    int maxseg, float* __restrict__ part) {
+    int maxseg, const float* __restrict__ ste_norms, float* __restrict__ part) {
   using Gm = AdjGeom<B>;
   constexpr int KS = Gm::KS, TT = Gm::TT, WS = Gm::WS, OWN = Gm::OWN, TILES = Gm::TILES;
   constexpr int S = Gm::S, STAGE = Gm::STAGE;
@@ -120,6 +124,10 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
     for (int a = 0; a < TT; ++a)
 #pragma unroll
       for (int o = 0; o < OWN; ++o) acc[a][o] = floatx16{};
+    // column norms n_j of this lane's source channels j = bB + 32 t2 + n
+    float nrm[OWN];
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) nrm[o] = STE ? ste_norms[b * B + 32 * (half * OWN + o) + n] : 0.f;
 
     // the load instructions of one tile into stage st (with WS waves sharing a
     // ring, wave `half` issues every WS-th of them)
@@ -165,8 +173,9 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
       const u32x4* LG = reinterpret_cast<const u32x4*>(sb + KS * 1024);
       const uint32_t* LB = reinterpret_cast<const uint32_t*>(sb + 2 * KS * 1024);
 
-      // transposed G and W for the owned column blocks: 16 rows per lane
-      u32x4 gT[OWN][2], wT[OWN][2];
+      // transposed G and W (and S = |W| n_j) for the owned column blocks:
+      // 16 rows per lane
+      u32x4 gT[OWN][2], wT[OWN][2], sT[OWN][2];
 #pragma unroll
       for (int o = 0; o < OWN; ++o) {
         const int t2 = half * OWN + o;
@@ -183,6 +192,12 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
                            pack2_exact(tg[8 * u + 4], tg[8 * u + 5]), pack2_exact(tg[8 * u + 6], tg[8 * u + 7])};
           wT[o][u] = u32x4{pack2_exact(tw[8 * u], tw[8 * u + 1]), pack2_exact(tw[8 * u + 2], tw[8 * u + 3]),
                            pack2_exact(tw[8 * u + 4], tw[8 * u + 5]), pack2_exact(tw[8 * u + 6], tw[8 * u + 7])};
+          if (STE) {
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[e] = __builtin_fabsf(tw[8 * u + e]) * nrm[o];
+            sT[o][u] = u32x4{pack2(sv[0], sv[1]), pack2(sv[2], sv[3]), pack2(sv[4], sv[5]), pack2(sv[6], sv[7])};
+          }
         }
       }
 #pragma unroll
@@ -223,6 +238,21 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
             acc[a][o] = mfma32(aop[u], gT[o][u], acc[a][o]);
             acc[a][o] = mfma32(yop[u], wT[o][u], acc[a][o]);
           }
+        if (STE) {
+          // (W_hat . Y), unmasked
+          u32x4 qop[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = wh[8 * u + e] * yy[8 * u + e];
+            qop[u] = u32x4{pack2(qv[0], qv[1]), pack2(qv[2], qv[3]), pack2(qv[4], qv[5]), pack2(qv[6], qv[7])};
+          }
+#pragma unroll
+          for (int o = 0; o < OWN; ++o)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) acc[a][o] = mfma32(qop[u], sT[o][u], acc[a][o]);
+        }
       }
     }
 
@@ -280,16 +310,17 @@ constexpr size_t adj_lds_bytes() {
 // fp32 VALU version: one thread per group of (j, k) outputs, rows streamed
 // through LDS one at a time; same persistent tile ranges and (workgroup,
 // segment) partial layout as the bf16 kernel.
-template <int B>
+template <int B, bool STE>
 __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restrict__ G,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ P,
                                                           const uint32_t* __restrict__ bits,
                                                           int cout, int cin, int tpw, int maxseg,
+                                                          const float* __restrict__ ste_norms,
                                                           float* __restrict__ part) {
   constexpr int PER = (B * B + 255) / 256;
   __shared__ float pb[B][B + 1];
-  __shared__ float wr[B], gr[B], am[B], ym[B];
+  __shared__ float wr[B], gr[B], am[B], ym[B], sw[B], qm[B];
   const int t = threadIdx.x;
   const int tpb = (cout + 31) / 32;
   const int total = (cin / B) * tpb;
@@ -310,8 +341,10 @@ __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restric
     for (int i = r0; i < r1; ++i) {
       __syncthreads();
       if (t < B) {
-        wr[t] = W[(size_t)i * cin + b * B + t];
+        const float wv = W[(size_t)i * cin + b * B + t];
+        wr[t] = wv;
         gr[t] = G[(size_t)i * cin + b * B + t];
+        if (STE) sw[t] = __builtin_fabsf(wv) * ste_norms[b * B + t];
       }
       __syncthreads();
       if (t < B) {
@@ -323,6 +356,7 @@ __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restric
         const uint32_t keep = (bits[((size_t)b * cout + i) * (B >> 5) + (t >> 5)] >> (t & 31)) & 1u;
         am[t] = keep ? s1 : 0.f;
         ym[t] = keep ? s2 : 0.f;
+        if (STE) qm[t] = s1 * s2;
       }
       __syncthreads();
 #pragma unroll
@@ -331,6 +365,7 @@ __global__ __launch_bounds__(256) void adjoint_f32_kernel(const float* __restric
         if (e < B * B) {
           const int j = e / B, k = e % B;
           acc[q] = fmaf(gr[j], am[k], fmaf(wr[j], ym[k], acc[q]));
+          if (STE) acc[q] = fmaf(sw[j], qm[k], acc[q]);
         }
       }
     }
@@ -359,13 +394,21 @@ AdjSplit adjoint_split(int cout, int cin, int B) {
   return sp;
 }
 
+template <int B, bool STE>
+static void adj_bf16(const uint16_t* G, const uint16_t* W, const u32x4* gfrag, const float* P, const uint32_t* bits,
+                     int cout, int cin, const AdjSplit& sp, const float* nrm, float* part, hipStream_t s) {
+  adjoint_bf16_kernel<B, STE><<<sp.grid, 256, adj_lds_bytes<B>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw,
+                                                                      sp.maxseg, nrm, part);
+}
+
 hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const u32x4* gfrag, const float* P,
                                const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
-                               float* part, hipStream_t s) {
+                               const float* ste_norms, float* part, hipStream_t s) {
+  const bool ste = ste_norms != nullptr;
   switch (B) {
-    case 32: adjoint_bf16_kernel<32><<<sp.grid, 256, adj_lds_bytes<32>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
-    case 64: adjoint_bf16_kernel<64><<<sp.grid, 256, adj_lds_bytes<64>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
-    case 128: adjoint_bf16_kernel<128><<<sp.grid, 256, adj_lds_bytes<128>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
+    case 32: (ste ? adj_bf16<32, true> : adj_bf16<32, false>)(G, W, gfrag, P, bits, cout, cin, sp, ste_norms, part, s); break;
+    case 64: (ste ? adj_bf16<64, true> : adj_bf16<64, false>)(G, W, gfrag, P, bits, cout, cin, sp, ste_norms, part, s); break;
+    case 128: (ste ? adj_bf16<128, true> : adj_bf16<128, false>)(G, W, gfrag, P, bits, cout, cin, sp, ste_norms, part, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -373,13 +416,20 @@ hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const u32x4
 
 // fp32 kernel: one workgroup per (block, 32-row tile range of one segment),
 // written in the same (workgroup, segment) partial layout as the bf16 kernel.
+template <int B, bool STE>
+static void adj_f32(const float* G, const float* W, const float* P, const uint32_t* bits, int cout, int cin,
+                    const AdjSplit& sp, const float* nrm, float* part, hipStream_t s) {
+  adjoint_f32_kernel<B, STE><<<sp.grid, 256, 0, s>>>(G, W, P, bits, cout, cin, sp.tpw, sp.maxseg, nrm, part);
+}
+
 hipError_t launch_adjoint_f32(const float* G, const float* W, const float* P,
                               const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
-                              float* part, hipStream_t s) {
+                              const float* ste_norms, float* part, hipStream_t s) {
+  const bool ste = ste_norms != nullptr;
   switch (B) {
-    case 32: adjoint_f32_kernel<32><<<sp.grid, 256, 0, s>>>(G, W, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
-    case 64: adjoint_f32_kernel<64><<<sp.grid, 256, 0, s>>>(G, W, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
-    case 128: adjoint_f32_kernel<128><<<sp.grid, 256, 0, s>>>(G, W, P, bits, cout, cin, sp.tpw, sp.maxseg, part); break;
+    case 32: (ste ? adj_f32<32, true> : adj_f32<32, false>)(G, W, P, bits, cout, cin, sp, ste_norms, part, s); break;
+    case 64: (ste ? adj_f32<64, true> : adj_f32<64, false>)(G, W, P, bits, cout, cin, sp, ste_norms, part, s); break;
+    case 128: (ste ? adj_f32<128, true> : adj_f32<128, false>)(G, W, P, bits, cout, cin, sp, ste_norms, part, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

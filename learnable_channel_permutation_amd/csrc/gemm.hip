@@ -23,14 +23,16 @@
 // padded output columns come out exactly zero.
 //
 // Epilogues: ERR stores C in bf16 and one sum of squares of the fp32
-// accumulators per workgroup (reduced later in a fixed order); DD scales by
-// -1/E (E read from device memory; 0 when E == 0) and stores bf16.
+// accumulators per workgroup (reduced later in a fixed order); ERRCOS also
+// writes one sum of Y . C per workgroup, Y a matrix of C's layout (the dense
+// layer outputs of the cosine objective); DD scales by a factor read from
+// device memory (written by the finalisation kernel) and stores bf16.
 #include "common.h"
 #include "kernels.h"
 
 namespace lcp {
 
-enum { EPI_ERR = 0, EPI_DD = 1 };
+enum { EPI_ERR = 0, EPI_DD = 1, EPI_ERRCOS = 2 };
 
 constexpr int GBK = 64;
 constexpr int GROUP_M = 4;
@@ -87,7 +89,7 @@ template <int BM, int BN, int EPI, int S>
 __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M,
     int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, float* __restrict__ part,
-    const float* __restrict__ Eptr) {
+    const float* __restrict__ Eptr, const uint16_t* __restrict__ Yc, float* __restrict__ part2) {
   constexpr int WM = BM / GWM, WN = BN / GWN, FM = WM / 32, FN = WN / 32;
   constexpr int AI = BM * 8 / GNT, BI = BN * 8 / GNT;     // 16-byte loads per thread per tile
   constexpr int STAGE = (BM + BN) * GBK;                   // bf16 elements per ring stage
@@ -178,12 +180,9 @@ __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
 
   // ---- epilogue: lane (h, ln) of block (i, j) holds row m0 + wm*WM + 32i + ln,
   // columns n0 + wn*WN + 32j + 16h + r, r < 16.
-  float scale = 1.f;
-  if (EPI == EPI_DD) {
-    const float E = *Eptr;
-    scale = (E > 0.f) ? -1.f / E : 0.f;
-  }
-  float ss = 0.f;
+  constexpr bool ERRS = EPI == EPI_ERR || EPI == EPI_ERRCOS;
+  const float scale = (EPI == EPI_DD) ? Eptr[1] : 1.f;
+  float ss = 0.f, sy = 0.f;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * WM + 32 * i + ln;
@@ -191,9 +190,18 @@ __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
     for (int j = 0; j < FN; ++j) {
       const int nb = n0 + wn * WN + 32 * j + 16 * h;
       const floatx16 a = acc[i][j];
-      if (EPI == EPI_ERR && m < M) {   // rows past M were read from a clamped row
+      if (ERRS && m < M) {   // rows past M were read from a clamped row
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss += a[r] * a[r];
+      }
+      if (EPI == EPI_ERRCOS && m < M && nb < N_store) {
+        const u32x4* ys = reinterpret_cast<const u32x4*>(Yc + (size_t)m * ldc + nb);
+        const u32x4 y0 = ys[0], y1 = ys[1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sy += lo_bf(y0[q]) * a[2 * q] + hi_bf(y0[q]) * a[2 * q + 1];
+          sy += lo_bf(y1[q]) * a[8 + 2 * q] + hi_bf(y1[q]) * a[8 + 2 * q + 1];
+        }
       }
       if (m < M && nb < N_store) {
         u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)m * ldc + nb);
@@ -204,17 +212,28 @@ __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
       }
     }
   }
-  if (EPI == EPI_ERR) {
+  if (ERRS) {
     __syncthreads();                                   // the ring is no longer read
     float* wsum = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) ss += shfl_xor(ss, x);
-    if (l == 0) wsum[w] = ss;
+    if (EPI == EPI_ERRCOS) {
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) sy += shfl_xor(sy, x);
+    }
+    if (l == 0) {
+      wsum[w] = ss;
+      wsum[GNW + w] = sy;
+    }
     __syncthreads();
     if (t == 0) {
-      float tot = 0.f;
-      for (int i = 0; i < GNW; ++i) tot += wsum[i];
+      float tot = 0.f, toty = 0.f;
+      for (int i = 0; i < GNW; ++i) {
+        tot += wsum[i];
+        toty += wsum[GNW + i];
+      }
       part[blockIdx.x] = tot;
+      if (EPI == EPI_ERRCOS) part2[blockIdx.x] = toty;
     }
   }
 }
@@ -228,7 +247,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        int N_valid, int N_store, int K,
                                                        float* __restrict__ C, int ldc,
                                                        float* __restrict__ part,
-                                                       const float* __restrict__ Eptr) {
+                                                       const float* __restrict__ Eptr,
+                                                       const float* __restrict__ Yc,
+                                                       float* __restrict__ part2) {
   __shared__ float as[16][64 + 1];
   __shared__ float bs[16][64 + 1];
   const int tiles_n = (N_store + 63) / 64;
@@ -254,43 +275,62 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
         for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(as[kk][ty * 4 + a], bs[kk][tx * 4 + c], acc[a][c]);
     __syncthreads();
   }
-  float scale = 1.f;
-  if (EPI == EPI_DD) {
-    const float E = *Eptr;
-    scale = (E > 0.f) ? -1.f / E : 0.f;
-  }
-  float ss = 0.f;
+  constexpr bool ERRS = EPI == EPI_ERR || EPI == EPI_ERRCOS;
+  const float scale = (EPI == EPI_DD) ? Eptr[1] : 1.f;
+  float ss = 0.f, sy = 0.f;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int m = m0 + ty * 4 + a, n = n0 + tx * 4 + c;
-      if (EPI == EPI_ERR) ss += acc[a][c] * acc[a][c];
-      if (m < M && n < N_store) C[(size_t)m * ldc + n] = acc[a][c] * scale;
+      if (ERRS) ss += acc[a][c] * acc[a][c];
+      if (m < M && n < N_store) {
+        C[(size_t)m * ldc + n] = acc[a][c] * scale;
+        if (EPI == EPI_ERRCOS) sy += Yc[(size_t)m * ldc + n] * acc[a][c];
+      }
     }
-  if (EPI == EPI_ERR) {
-    __shared__ float wsum[4];
+  if (ERRS) {
+    __shared__ float wsum[8];
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) ss += shfl_xor(ss, x);
-    if ((t & 63) == 0) wsum[t >> 6] = ss;
+    if (EPI == EPI_ERRCOS) {
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) sy += shfl_xor(sy, x);
+    }
+    if ((t & 63) == 0) {
+      wsum[t >> 6] = ss;
+      wsum[4 + (t >> 6)] = sy;
+    }
     __syncthreads();
-    if (t == 0) part[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    if (t == 0) {
+      part[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+      if (EPI == EPI_ERRCOS) part2[blockIdx.x] = (wsum[4] + wsum[5]) + (wsum[6] + wsum[7]);
+    }
   }
 }
 
 // E = sqrt(sum of partials), summed in a fixed order by one wave: lane l adds
 // part[l], part[l + 64], ... in order, then the lanes are combined by a fixed
-// butterfly.
+// butterfly. E_ws[0] = E and E_ws[1] = -1/E (0 when E == 0), the factor the
+// dD epilogue applies (dE/dR = R / E, dE/dW_tilde = -(R / E) X). With
+// sum_only the plain sum is written to err (E_ws unused).
 __global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restrict__ part, int n,
                                                             float* __restrict__ E_ws,
-                                                            float* __restrict__ err) {
+                                                            float* __restrict__ err, int sum_only) {
   float s = 0.f;
   for (int i = threadIdx.x; i < n; i += 64) s += part[i];
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) s += shfl_xor(s, x);
   if (threadIdx.x == 0) {
+    if (sum_only) {
+      *err = s;
+      return;
+    }
     const float E = sqrtf(s);
-    if (E_ws) *E_ws = E;
+    if (E_ws) {
+      E_ws[0] = E;
+      E_ws[1] = (E > 0.f) ? -1.f / E : 0.f;
+    }
     if (err) *err = E;
   }
 }
@@ -308,10 +348,14 @@ int gemm_error_parts(int M, int N, int bf16) {
 
 hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
                                   int N_valid, int N_store, int K, uint16_t* C, int ldc,
-                                  float* part, hipStream_t s) {
+                                  float* part, const uint16_t* Y, float* party, hipStream_t s) {
   const int G = gemm_error_parts(M, N_store, 1);
-  gemm_bf16_kernel<EBM, EBN, EPI_ERR, ES><<<G, GNT, gemm_lds_bytes<EBM, EBN, ES>(), s>>>(
-      A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr);
+  if (Y)
+    gemm_bf16_kernel<EBM, EBN, EPI_ERRCOS, ES><<<G, GNT, gemm_lds_bytes<EBM, EBN, ES>(), s>>>(
+        A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr, Y, party);
+  else
+    gemm_bf16_kernel<EBM, EBN, EPI_ERR, ES><<<G, GNT, gemm_lds_bytes<EBM, EBN, ES>(), s>>>(
+        A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -319,28 +363,38 @@ hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, i
                                int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s) {
   const int G = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
   gemm_bf16_kernel<DBM, DBN, EPI_DD, DS><<<G, GNT, gemm_lds_bytes<DBM, DBN, DS>(), s>>>(
-      A, lda, Bm, ldb, M, N, N, K, C, ldc, nullptr, E);
+      A, lda, Bm, ldb, M, N, N, K, C, ldc, nullptr, E, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_error_f32(const float* A, int lda, const float* Bm, int ldb, int M,
                                  int N_valid, int N_store, int K, float* C, int ldc, float* part,
-                                 hipStream_t s) {
+                                 const float* Y, float* party, hipStream_t s) {
   const int G = gemm_error_parts(M, N_store, 0);
-  gemm_f32_kernel<EPI_ERR, 0><<<G, 256, 0, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr);
+  if (Y)
+    gemm_f32_kernel<EPI_ERRCOS, 0><<<G, 256, 0, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part,
+                                                      nullptr, Y, party);
+  else
+    gemm_f32_kernel<EPI_ERR, 0><<<G, 256, 0, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part,
+                                                   nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dd_f32(const float* R, int ldr, const float* X, int ldx, int M, int N,
                               int K, const float* E, float* C, int ldc, hipStream_t s) {
   const int G = gemm_error_parts(M, N, 0);
-  gemm_f32_kernel<EPI_DD, 1><<<G, 256, 0, s>>>(R, ldr, X, ldx, M, N, N, K, C, ldc, nullptr, E);
+  gemm_f32_kernel<EPI_DD, 1><<<G, 256, 0, s>>>(R, ldr, X, ldx, M, N, N, K, C, ldc, nullptr, E, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_error_finalize(const float* part, int nparts, float* E_ws, float* err,
                                  hipStream_t s) {
-  error_finalize_kernel<<<1, 64, 0, s>>>(part, nparts, E_ws, err);
+  error_finalize_kernel<<<1, 64, 0, s>>>(part, nparts, E_ws, err, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_finalize(const float* part, int nparts, float* out, hipStream_t s) {
+  error_finalize_kernel<<<1, 64, 0, s>>>(part, nparts, nullptr, out, 1);
   return hipGetLastError();
 }
 

@@ -77,34 +77,51 @@ hipError_t launch_diff(const void* W, const void* Wt, int n, int bf16, void* D, 
 
 // GEMMs (gemm.hip). C[m][n] = sum_k A[m][k] B[n][k].
 // Error epilogue: store C (bf16 or f32, ldc) for n < n_store and write one
-// partial sum of squares per workgroup to part[]; returns the number of
-// partials through *nparts (host computed).
+// partial sum of squares per workgroup to part[] (gemm_error_parts of them).
+// With Y non-null (a matrix of C's layout and ldc) it also writes one partial
+// of sum Y . C per workgroup to party[].
 int gemm_error_parts(int M, int N, int bf16);
 hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
                                   int N_valid, int N_store, int K, uint16_t* C, int ldc,
-                                  float* part, hipStream_t s);
+                                  float* part, const uint16_t* Y, float* party, hipStream_t s);
 hipError_t launch_gemm_error_f32(const float* A, int lda, const float* Bm, int ldb, int M,
                                  int N_valid, int N_store, int K, float* C, int ldc, float* part,
-                                 hipStream_t s);
-// dD epilogue: C = -(1/E) * acc, with E read from device memory (0 -> 0).
+                                 const float* Y, float* party, hipStream_t s);
+// dD epilogue: C = coef[1] * acc, coef in device memory (written by a
+// finalisation kernel: -1/E for the Frobenius objective, 1 for the cosine).
 hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
-                               int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s);
-// f32 dD: C[m][n] = -(1/E) sum_t R[m][t] X[t][n]  (X row-major [K][N]).
+                               int N, int K, const float* coef, uint16_t* C, int ldc, hipStream_t s);
+// f32 dD: C[m][n] = coef[1] sum_t R[m][t] X[t][n]  (X row-major [K][N]).
 hipError_t launch_gemm_dd_f32(const float* R, int ldr, const float* X, int ldx, int M, int N,
-                              int K, const float* E, float* C, int ldc, hipStream_t s);
+                              int K, const float* coef, float* C, int ldc, hipStream_t s);
+// E = sqrt(sum part) to err and E_ws[0]; E_ws[1] = -1/E (0 when E == 0).
 hipError_t launch_error_finalize(const float* part, int nparts, float* E_ws, float* err,
                                  hipStream_t s);
+// out = sum part (fixed order).
+hipError_t launch_sum_finalize(const float* part, int nparts, float* out, hipStream_t s);
+
+// Cosine objective (cosine.hip). From r = sum part (||R||^2), a = sum party
+// (<Y, R>) and y2 = ||Y||^2 with R = Y - Y~: err = 1 - <Y, Y~> / (|Y| |Y~|),
+// coef[0] = sqrt(r), coef[1] = 1 (dD factor), coef[2], coef[3] = the
+// coefficients of Y and R in dL/dY~ (all zero when |Y| |Y~| == 0).
+hipError_t launch_cosine_finalize(const float* part, const float* party, int nparts, const float* y2,
+                                  float* coef, float* err, hipStream_t s);
+// dY~ = coef[2] Y + coef[3] R over n elements (n % 8 == 0, 16-byte aligned).
+hipError_t launch_cosine_grad(const void* Y, const void* R, size_t n, int bf16, const float* coef, void* out,
+                              hipStream_t s);
 
 // Block adjoint (adjoint.hip). Workgroup g of the fixed grid takes tiles
 // [g*tpw, (g+1)*tpw) of the block-major 32-row tile sequence (tpb per block)
 // and writes one partial B x B matrix per block it touches to
 // part[(g * maxseg + (block - first block of g)) * B * B].
 AdjSplit adjoint_split(int cout, int cin, int B);
+// ste_norms non-null adds the straight-through term of the mask,
+// S_b^T ((G_b P_b) . (W_b P_b)) with S = |W| . ste_norms[col].
 hipError_t launch_adjoint_bf16(const uint16_t* G, const uint16_t* W, const u32x4* gfrag, const float* P,
                                const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
-                               float* part, hipStream_t s);
+                               const float* ste_norms, float* part, hipStream_t s);
 hipError_t launch_adjoint_f32(const float* G, const float* W, const float* P,
                               const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
-                              float* part, hipStream_t s);
+                              const float* ste_norms, float* part, hipStream_t s);
 
 }  // namespace lcp

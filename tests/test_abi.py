@@ -116,11 +116,15 @@ def test_invalid_arguments_return_codes_without_launching():
     assert lib.lcp_error(p, p, p, L.LCP_BF16, 8, 64, 16, p, None, _fake(0x100010), n, s) == L.LCP_E_WORKSPACE
 
 
+def _lay(L, W, X, Xt, norms, dtype, cout, cin, T, B, Y=0, y2=0):
+    return L.lcp_layer(W=W, X=X, Xt=Xt, norms=norms, Y=Y, y2=y2, dtype=dtype, cout=cout, cin=cin, T=T, B=B)
+
+
 def test_step_argument_validation():
     L = _lib()
     lib = L.LIB
     p = 0x100000
-    layer = L.lcp_layer(p, p, p, p, L.LCP_BF16, 64, 128, 32, 64)
+    layer = _lay(L, p, p, p, p, L.LCP_BF16, 64, 128, 32, 64)
     cfg = L.lcp_cfg(5, 1.0, 2, 4)
     ws = ctypes.c_void_p(p)
     need = L.lcp_step_workspace_bytes(64, 128, 32, 64, 5, L.LCP_BF16)
@@ -143,11 +147,27 @@ def test_step_argument_validation():
     assert fwd(cfg=L.lcp_cfg(5, 1.0, 0, 4)) == L.LCP_E_INVAL
     assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 16)) in (L.LCP_E_UNSUPPORTED, L.LCP_E_INVAL)
     assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 3)) == L.LCP_E_INVAL           # B % M
-    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 64, 96, 32, 64)) == L.LCP_E_INVAL   # cin % B
-    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 64, 96, 32, 96)) == L.LCP_E_UNSUPPORTED
-    assert fwd(layer=L.lcp_layer(p, p, p, p, 5, 64, 128, 32, 64)) == L.LCP_E_UNSUPPORTED
-    assert fwd(layer=L.lcp_layer(0, p, p, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL
-    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 0, 128, 32, 64)) == L.LCP_E_INVAL
-    assert fwd(layer=L.lcp_layer(p, p, p, p, L.LCP_BF16, 1 << 20, 1 << 12, 32, 64)) == L.LCP_E_INVAL
-    assert bwd(layer=L.lcp_layer(p, p, 0, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL   # bf16 needs Xt
+    assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 64, 96, 32, 64)) == L.LCP_E_INVAL   # cin % B
+    assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 64, 96, 32, 96)) == L.LCP_E_UNSUPPORTED
+    assert fwd(layer=_lay(L, p, p, p, p, 5, 64, 128, 32, 64)) == L.LCP_E_UNSUPPORTED
+    assert fwd(layer=_lay(L, 0, p, p, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL
+    assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 0, 128, 32, 64)) == L.LCP_E_INVAL
+    assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 1 << 20, 1 << 12, 32, 64)) == L.LCP_E_INVAL
+    assert bwd(layer=_lay(L, p, p, 0, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL   # bf16 needs Xt
     assert bwd(n=need - 256) == L.LCP_E_WORKSPACE
+    # objective and straight-through options
+    assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 4, 0, 2, 0)) == L.LCP_E_INVAL            # unknown loss
+    assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 4, 0, 0, 2)) == L.LCP_E_INVAL            # mask_ste not 0/1
+    cos = L.lcp_cfg(5, 1.0, 2, 4, 0, L.LCP_LOSS_COSINE, 1)
+    assert fwd(cfg=cos) == L.LCP_E_INVAL                                         # cosine needs Y, y2
+    assert fwd(cfg=cos, layer=_lay(L, p, p, p, p, L.LCP_BF16, 64, 128, 32, 64, Y=p)) == L.LCP_E_INVAL
+    assert fwd(cfg=cos, layer=_lay(L, p, p, p, p, L.LCP_BF16, 64, 128, 32, 64, Y=p + 8, y2=p)) == L.LCP_E_INVAL
+    assert bwd(cfg=cos) == L.LCP_E_INVAL
+    # layer outputs of the cosine objective
+    s = None
+    en = ctypes.c_size_t(1 << 20)
+    assert lib.lcp_layer_outputs(p, p, L.LCP_BF16, 8, 64, 16, None, p, p, en, s) == L.LCP_E_INVAL
+    assert lib.lcp_layer_outputs(p, p, L.LCP_BF16, 8, 64, 16, p, None, p, en, s) == L.LCP_E_INVAL
+    assert lib.lcp_layer_outputs(p, p, L.LCP_BF16, 8, 48, 16, p, p, p, en, s) == L.LCP_E_INVAL
+    assert lib.lcp_layer_outputs(p, p, 9, 8, 64, 16, p, p, p, en, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_layer_outputs(p, p, L.LCP_BF16, 8, 64, 16, p, p, p, ctypes.c_size_t(16), s) == L.LCP_E_WORKSPACE
