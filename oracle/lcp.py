@@ -46,7 +46,8 @@ __all__ = [
     "nm_mask", "pack_bits", "unpack_bits", "unpermute_diff", "pruning_error",
     "step_forward", "step_backward", "sinkhorn_adjoint", "block_adjoint",
     "harden", "adamw", "tau_schedule", "train", "layer_output", "cosine_loss",
-    "cosine_grad", "mask_ste_adjoint",
+    "cosine_grad", "mask_ste_adjoint", "perm_from_hard", "gather_channels", "sparse_pack",
+    "deploy_forward",
 ]
 
 
@@ -409,3 +410,57 @@ def train(W, X, logits, steps, lr, N, M, iters, hard=True, tau0=1.0, tau1=0.1,
         lg, m, v = adamw(lg, g, m, v, t + 1, lr, **adam)
     return lg, errs
 
+
+
+# deploy: inference with the learned permutation ------------------------------
+def perm_from_hard(P):
+    """perm[b][k] = the source row j with P_b[j, k] = 1, for a hard P
+    ([nb, B, B] 0/1 with one 1 per row and column). int64 [nb, B]."""
+    P = _f64(P)
+    if not np.all((P == 0.0) | (P == 1.0)) or not np.all(P.sum(axis=1) == 1.0) \
+            or not np.all(P.sum(axis=2) == 1.0):
+        raise ValueError("P is not a block permutation")
+    return np.argmax(P, axis=1)
+
+
+def gather_channels(X, P):
+    """Activations in permuted channel order for a hard P: X P_B, so column
+    bB + k holds X[:, bB + perm[b][k]] (PermLLM summary, inference
+    acceleration: the channel permutation applied at inference time)."""
+    perm_from_hard(P)
+    return block_permute(X, P)
+
+
+def sparse_pack(A, N, M):
+    """Compressed form of a matrix with at most N nonzeros in every group of
+    M consecutive columns: vals [rows, cin/M*N] holds each group's kept
+    entries in ascending position, pos [rows, cin/M, N] their positions in
+    the group. Groups with fewer than N nonzeros are completed with zero
+    entries at the lowest free positions. Here "kept" means nonzero."""
+    A = _f64(A)
+    rows, cin = A.shape
+    if cin % M:
+        raise ValueError("columns must be a multiple of M")
+    G = cin // M
+    vals = np.zeros((rows, G * N))
+    pos = np.zeros((rows, G, N), dtype=np.int64)
+    for i in range(rows):
+        for g in range(G):
+            seg = A[i, g * M:(g + 1) * M]
+            nz = [k for k in range(M) if seg[k] != 0.0]
+            if len(nz) > N:
+                raise ValueError("group with more than N nonzeros")
+            free = [k for k in range(M) if k not in nz]
+            chosen = sorted(nz + free[:N - len(nz)])
+            for s, k in enumerate(chosen):
+                pos[i, g, s] = k
+                vals[i, g * N + s] = seg[k]
+    return vals, pos
+
+
+def deploy_forward(W, X, P, mask):
+    """Layer outputs of the deployed sparse layer, Y = X W_tilde^T (T x Cout)
+    with W_tilde = ((W P_B) . M) P_B^T the pruned weight in source order."""
+    W_hat = block_permute(W, P)
+    _, W_tilde, _ = unpermute_diff(W, W_hat, mask, P)
+    return _f64(X) @ W_tilde.T

@@ -727,6 +727,77 @@ def pin_training_cosine(o):
     assert final < wanda, (final, wanda)
 
 
+# ------------------------------------------------------------------- deploy --
+def _hard_case(seed, cout=6, cin=16, T=5, B=8):
+    rng = _rng(seed)
+    W = rng.standard_normal((cout, cin))
+    X = rng.standard_normal((T, cin))
+    nb = cin // B
+    perm = np.stack([rng.permutation(B) for _ in range(nb)])
+    P = np.zeros((nb, B, B))
+    for b in range(nb):
+        P[b, perm[b], np.arange(B)] = 1.0          # position k takes source row perm[b][k]
+    return W, X, P, perm
+
+
+def pin_deploy_forms(o):
+    """The deployed layer three ways, for a hard P and its N:M mask: the
+    definition X W_tilde^T; permuted activations times the N:M-sparse
+    permuted weight (the inference form); and X times W with the mask moved
+    back to source positions by explicit loops."""
+    for seed, (N, M) in ((40, (2, 4)), (41, (4, 8)), (42, (1, 4))):
+        W, X, P, perm = _hard_case(seed)
+        cout, cin = W.shape
+        B = P.shape[1]
+        fw = o.step_forward(W, X, None, 1.0, 1, N, M, P=P)
+        mask = fw["mask"]
+        Y = o.deploy_forward(W, X, P, mask)
+        Ws = o.block_permute(W, P) * mask
+        Y2 = o.gather_channels(X, P) @ Ws.T
+        Morig = np.zeros((cout, cin))
+        for i in range(cout):
+            for b in range(cin // B):
+                for k in range(B):
+                    Morig[i, b * B + perm[b][k]] = mask[i, b * B + k]
+        Y3 = X @ (W * Morig).T
+        assert np.allclose(Y, Y2, rtol=1e-13, atol=1e-13)
+        assert np.allclose(Y, Y3, rtol=1e-13, atol=1e-13)
+        assert np.sum(Morig) == cout * cin * N // M
+
+
+def pin_gather_is_index_select(o):
+    """gather_channels equals numpy fancy indexing with the global source
+    index of every position; perm_from_hard recovers the permutation."""
+    W, X, P, perm = _hard_case(43, cin=24, B=8)
+    B = P.shape[1]
+    g = np.concatenate([b * B + perm[b] for b in range(perm.shape[0])])
+    assert np.array_equal(o.perm_from_hard(P), perm)
+    assert np.array_equal(o.gather_channels(X, P), X[:, g])
+
+
+def pin_sparse_pack(o):
+    """Compressed N:M storage: decoding vals and positions gives the matrix
+    back exactly, positions ascend inside each group, and groups with fewer
+    nonzeros are completed with zeros at the lowest free positions."""
+    rng = _rng(44)
+    for N, M in ((2, 4), (4, 8), (1, 4)):
+        A = rng.standard_normal((5, 32))
+        keep = o.nm_mask(np.abs(A), N, M)
+        A = A * keep
+        vals, pos = o.sparse_pack(A, N, M)
+        back = np.zeros_like(A)
+        for i in range(A.shape[0]):
+            for g in range(A.shape[1] // M):
+                assert list(pos[i, g]) == sorted(pos[i, g]) and len(set(pos[i, g])) == N
+                for s in range(N):
+                    back[i, g * M + pos[i, g, s]] += vals[i, g * N + s]
+        assert np.array_equal(back, A)
+    Z = np.zeros((1, 4))
+    Z[0, 2] = 5.0
+    vals, pos = o.sparse_pack(Z, 2, 4)
+    assert list(pos[0, 0]) == [0, 2] and list(vals[0]) == [0.0, 5.0]
+
+
 ALL_PINS = [
     pin_sinkhorn_2x2_golden, pin_sinkhorn_uniform, pin_sinkhorn_closed_form,
     pin_sinkhorn_closed_form_values, pin_sinkhorn_doubly_stochastic,
@@ -740,5 +811,6 @@ ALL_PINS = [
     pin_hard_forward_planted, pin_straight_through_gradient_fd, pin_adamw_torch,
     pin_tau_schedule, pin_training_beats_wanda, pin_cosine_closed_forms,
     pin_cosine_dense_is_zero, pin_cosine_gradient_fd, pin_cosine_grad_geometry,
-    pin_mask_ste_fd, pin_mask_ste_hard_dP_fd, pin_training_cosine,
+    pin_mask_ste_fd, pin_mask_ste_hard_dP_fd, pin_training_cosine, pin_deploy_forms,
+    pin_gather_is_index_select, pin_sparse_pack,
 ]

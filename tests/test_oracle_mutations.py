@@ -254,6 +254,25 @@ def _train_ignores_loss(W, X, logits, steps, lr, N, M, iters, hard=True, loss="f
     return _orig["train"](W, X, logits, steps, lr, N, M, iters, hard=hard, mask_ste=mask_ste, **kw)
 
 
+def _gather_inverse(X, P):
+    return _orig["gather_channels"](X, np.transpose(np.asarray(P, dtype=np.float64), (0, 2, 1)))
+
+
+def _pack_descending(A, N, M):
+    vals, pos = _orig["sparse_pack"](A, N, M)
+    rows, G = pos.shape[0], pos.shape[1]
+    return vals.reshape(rows, G, N)[:, :, ::-1].reshape(rows, G * N), pos[:, :, ::-1]
+
+
+def _deploy_unmasked(W, X, P, mask):
+    return _orig["deploy_forward"](W, X, P, np.ones_like(np.asarray(mask, dtype=np.float64)))
+
+
+def _deploy_permuted_order(W, X, P, mask):
+    Ws = olcp.block_permute(W, P) * np.asarray(mask, dtype=np.float64)
+    return np.asarray(X, dtype=np.float64) @ Ws.T
+
+
 MUTATIONS = [
     ("sinkhorn", _sinkhorn_cols_first),
     ("sinkhorn", _sinkhorn_times_tau),
@@ -298,6 +317,10 @@ MUTATIONS = [
     ("mask_ste_adjoint", _ste_unpermuted_weight),
     ("step_backward", _ste_mask_term_at_soft_P),
     ("train", _train_ignores_loss),
+    ("gather_channels", _gather_inverse),
+    ("sparse_pack", _pack_descending),
+    ("deploy_forward", _deploy_unmasked),
+    ("deploy_forward", _deploy_permuted_order),
 ]
 
 # the full 8! enumeration is covered by the plain pin run; the rest are fast
