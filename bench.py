@@ -51,6 +51,8 @@ def parse():
                          "part of the per-layer setup of every step)")
     ap.add_argument("--mask-ste", action="store_true",
                     help="straight-through gradient of the mask in the backward (another workload)")
+    ap.add_argument("--deploy", action="store_true",
+                    help="deploy path of a trained layer: channel gather + 2:4 sparse GEMM (another workload)")
     ap.add_argument("--adamw", action="store_true",
                     help="training step: the backward with the fused AdamW update of the logits")
     ap.add_argument("--saturate", action="store_true",
@@ -151,6 +153,120 @@ def cpu_baseline(spec, lay, hard=False, loss="frobenius", mask_ste=False):
                       % ("forward+backward" if spec.backward else "forward", spec.cout, spec.cin, spec.T, dt)}
 
 
+def cpu_baseline_deploy(W, X, P, mask):
+    """The float64 oracle's deployed-layer forward on the host cores (one
+    full forward of the same layer is the sample)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    oracle.deploy_forward(W, X, P, mask)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "forwards/s", "cores": int(cores), "kind": "oracle",
+            "sample": "one full deployed-layer forward (%dx%d weight, %d tokens), float64 NumPy, %.1f s"
+                      % (W.shape[0], W.shape[1], X.shape[0], dt)}
+
+
+def run_deploy(args, torch, lcp, lcp_synth):
+    """Deploy workload: Y = gather(X) Ws^T with the 2:4 packed weight, on the
+    bench layer's shape (weight 4096 x 11008, 2048 tokens, B = 64)."""
+    L = lcp._lib
+    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    cout, cin, T, B = spec.cout, spec.cin, spec.T, spec.B
+    lay = lcp_synth.make_layer(spec)
+    dev = torch.device("cuda:0")
+    rng = np.random.Generator(np.random.PCG64(2024))
+    nb = cin // B
+    perm_np = np.stack([rng.permutation(B) for _ in range(nb)]).astype(np.int32)
+    W = torch.from_numpy(lay.W).to(dev).to(torch.bfloat16)
+    X = torch.from_numpy(lay.X).to(dev).to(torch.bfloat16)
+    perm = torch.from_numpy(perm_np).to(dev)
+    # a 2:4 mask in permuted positions from seeded random scores
+    scores = torch.from_numpy(rng.random((cout, cin), dtype=np.float32)).to(dev)
+    bits = torch.empty((cout, cin // 32), dtype=torch.int32, device=dev)
+    L.lcp_nm_mask(scores, 2, 4, bits)
+    vb, mb = L.lcp_sparse_pack_bytes(cout, cin)
+    vals = torch.empty(vb, dtype=torch.uint8, device=dev)
+    meta = torch.empty(mb, dtype=torch.uint8, device=dev)
+    L.lcp_sparse_pack(W, B, perm, bits, vals, meta)
+    Xp = torch.empty_like(X)
+    Y = torch.empty((T, cout), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        L.lcp_deploy_forward(vals, meta, perm, B, X, cout, Xp, Y)
+    torch.cuda.synchronize()
+    K = args.steps
+    he = HipEvents()
+    ev = [(he.new(), he.new(), he.new()) for _ in range(K)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(K):
+        he.record(ev[k][0], stream)
+        L.lcp_gather_channels(X, B, perm, Xp)
+        he.record(ev[k][1], stream)
+        L.lcp_sparse_gemm(vals, meta, Xp, cout, Y)
+        he.record(ev[k][2], stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_stop) / K
+    g_ms = sum(he.ms(a, b) for a, b, _ in ev) / K
+    s_ms = sum(he.ms(b, c) for _, b, c in ev) / K
+    he.close()
+    # context on the same box: PyTorch's own gather and dense bf16 GEMM
+    gidx = torch.from_numpy((np.arange(nb)[:, None] * B + perm_np).reshape(-1).astype(np.int64)).to(dev)
+    Wd = W.contiguous()
+    for _ in range(3):
+        torch.index_select(X, 1, gidx)
+        torch.matmul(X, Wd.t())
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    for _ in range(reps):
+        torch.index_select(X, 1, gidx)
+    e1.record(stream)
+    for _ in range(reps):
+        torch.matmul(X, Wd.t())
+    e2.record(stream)
+    torch.cuda.synchronize()
+    torch_gather_ms = e0.elapsed_time(e1) / reps
+    torch_dense_ms = e1.elapsed_time(e2) / reps
+    useful = 2.0 * T * cout * (cin // 2)          # nonzero multiply-adds of the 2:4 weight
+    achieved = useful / (s_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        P = np.zeros((nb, B, B))
+        for b in range(nb):
+            P[b, perm_np[b], np.arange(B)] = 1.0
+        import oracle
+        mask = oracle.unpack_bits(bits.cpu().numpy().view(np.uint32), cin)
+        cpu = cpu_baseline_deploy(lay.W, lay.X, P, mask)
+    gather_bytes = 2.0 * 2 * T * cin
+    out = {
+        "metric": "LCP deployed-layer forwards/sec (%dx%d 2:4, %d tokens)" % (cout, cin, T),
+        "value": round(1000.0 / ms, 2),
+        "unit": "forwards/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded LLaMA-shaped layer, random block permutation and 2:4 mask)",
+        "config": {"workload": "lcp_deploy_forward", "layer": spec.name, "cout": cout, "cin": cin, "T": T,
+                   "B": B, "N": 2, "M": 4},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("sparse_gemm"),
+                     "kernel": "sparse_gemm", "kernel_ms": round(s_ms, 4),
+                     "note": "flops = nonzero multiply-adds x 2, priced against the dense bf16 peak"},
+        "gather": {"ms": round(g_ms, 4), "GB/s": round(gather_bytes / (g_ms * 1e-3) / 1e9, 1)},
+        "context": {"torch_index_select_ms": round(torch_gather_ms, 4),
+                    "torch_dense_matmul_ms": round(torch_dense_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def saturating_kernels(lcp, torch, he):
     """Sinkhorn forward over all B = 64 blocks of a LLaMA-7B-shaped model's
     projection layers (17,792 blocks) and lcp_nm_mask on 28672 x 8192 fp32
@@ -208,6 +324,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.deploy:
+        run_deploy(args, torch, lcp, lcp_synth)
+        return
 
     ci = lcp_synth.BENCH_CONFIG if args.config is None else args.config
     spec = lcp_synth.CONFIGS[ci]

@@ -300,6 +300,56 @@ int lcp_train(const lcp_layer* L, float* logits, const lcp_cfg* c, void* ws,
               size_t ws_bytes, float* m, float* v, int steps, float tau0,
               float tau1, const lcp_adamw_cfg* oc, float* errs, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Deploy path of a trained layer ([PermLLM] inference acceleration: a
+ * channel-permutation kernel applied to the activations at inference time and
+ * the N:M-sparse layer). With the hard permutation perm ([nb][B] int32,
+ * perm[b][k] = source channel of position bB + k, as lcp_harden writes it)
+ * and the 2:4 mask in permuted positions (bits, [cout][cin/32] uint32 as
+ * lcp_step_fwd's bits_out), the deployed layer computes
+ *   Y = Xp Ws^T,  Xp[t][bB+k] = X[t][bB+perm[b][k]],  Ws = (W P_B) . M,
+ * which equals X W_tilde^T. BF16 only; 2:4 only (the sparse matrix cores'
+ * format); cout % 32 == 0, cin % 32 == 0, cin % B == 0. perm entries are
+ * read modulo B (B is a power of two), so every access stays inside its
+ * block; an entry that is not a permutation gives a wrong but bounded result.
+ *
+ * Packed weights (opaque to callers; produced by lcp_sparse_pack): vals
+ * holds, per 32-row x 32-position fragment, the 64 lane operands of the
+ * gfx950 sparse MFMA (each lane: one row, 16 positions, the 2 kept values of
+ * each group of 4, lower position first); meta holds the 2-bit positions,
+ * 16 bits per lane and fragment, two fragments per uint32.
+ */
+int lcp_sparse_pack_bytes(int cout, int cin, size_t* vals_bytes,
+                          size_t* meta_bytes);
+
+/* lcp_sparse_pack - pack W (bf16 [cout][cin]) permuted by perm and masked by
+ * bits into (vals, meta). Groups of 4 whose mask does not keep exactly 2
+ * positions are packed with their first two kept positions, completed by
+ * the lowest free positions with value 0. vals 16-byte aligned, meta 4-byte
+ * aligned, sizes from lcp_sparse_pack_bytes. */
+int lcp_sparse_pack(const void* W, int cout, int cin, int B,
+                    const int32_t* perm, const uint32_t* bits, void* vals,
+                    uint32_t* meta, void* stream);
+
+/* lcp_gather_channels - Xp[t][bB+k] = X[t][bB+perm[b][k]] (bf16 [T][cin]
+ * both; Xp 16-byte aligned, not aliasing X): the channel permutation of the
+ * activations. */
+int lcp_gather_channels(const void* X, int T, int cin, int B,
+                        const int32_t* perm, void* Xp, void* stream);
+
+/* lcp_sparse_gemm - Y[t][o] = sum_k Ws[o][k] Xp[t][k] on the 2:4 sparse
+ * matrix cores: Xp bf16 [T][cin], Y bf16 [T][cout] (fp32 accumulation, one
+ * rounding), vals/meta from lcp_sparse_pack. Y, Xp, vals 16-byte aligned. */
+int lcp_sparse_gemm(const void* vals, const uint32_t* meta, const void* Xp,
+                    int T, int cout, int cin, void* Y, void* stream);
+
+/* lcp_deploy_forward - lcp_gather_channels into the caller's buffer Xp
+ * (bf16 [T][cin]) followed by lcp_sparse_gemm: the deployed layer's output
+ * Y (bf16 [T][cout]) for activations X (bf16 [T][cin]). */
+int lcp_deploy_forward(const void* vals, const uint32_t* meta,
+                       const int32_t* perm, int B, const void* X, int T,
+                       int cout, int cin, void* Xp, void* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

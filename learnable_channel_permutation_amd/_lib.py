@@ -32,7 +32,8 @@ EXPORTS = [
     "lcp_xt_pitch", "lcp_layer_init", "lcp_permute", "lcp_nm_mask",
     "lcp_error_workspace_bytes", "lcp_error", "lcp_step_workspace_bytes", "lcp_step_fwd",
     "lcp_step_bwd", "lcp_harden", "lcp_adamw", "lcp_step_bwd_adamw", "lcp_train",
-    "lcp_layer_outputs",
+    "lcp_layer_outputs", "lcp_sparse_pack_bytes", "lcp_sparse_pack", "lcp_gather_channels",
+    "lcp_sparse_gemm", "lcp_deploy_forward",
 ]
 
 
@@ -90,6 +91,11 @@ def _load():
         "lcp_error_workspace_bytes": (i, [i, i, i, i, psz]),
         "lcp_error": (i, [vp, vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
         "lcp_layer_outputs": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
+        "lcp_sparse_pack_bytes": (i, [i, i, psz, psz]),
+        "lcp_sparse_pack": (i, [vp, i, i, i, vp, vp, vp, vp, vp]),
+        "lcp_gather_channels": (i, [vp, i, i, i, vp, vp, vp]),
+        "lcp_sparse_gemm": (i, [vp, vp, vp, i, i, i, vp, vp]),
+        "lcp_deploy_forward": (i, [vp, vp, vp, i, vp, i, i, i, vp, vp, vp]),
         "lcp_step_workspace_bytes": (i, [i, i, i, i, i, i, psz]),
         "lcp_step_fwd": (i, [ctypes.POINTER(lcp_layer), vp, ctypes.POINTER(lcp_cfg), vp, sz, vp, vp, vp,
                              ctypes.POINTER(lcp_timing), vp]),
@@ -267,3 +273,34 @@ def lcp_train(layer, logits, cfg, ws, m, v, steps, tau0, tau1, acfg, errs, strea
                                              float(tau0), float(tau1), ctypes.byref(acfg), _p(errs),
                                              _stream(stream)))
 
+
+
+# ---- deploy path ------------------------------------------------------------
+def lcp_sparse_pack_bytes(cout, cin):
+    vb, mb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("lcp_sparse_pack_bytes", LIB.lcp_sparse_pack_bytes(cout, cin, ctypes.byref(vb), ctypes.byref(mb)))
+    return vb.value, mb.value
+
+
+def lcp_sparse_pack(W, B, perm, bits, vals, meta, stream=None):
+    cout, cin = W.shape
+    return _check("lcp_sparse_pack", LIB.lcp_sparse_pack(_p(W), cout, cin, int(B), _p(perm), _p(bits), _p(vals),
+                                                         _p(meta), _stream(stream)))
+
+
+def lcp_gather_channels(X, B, perm, Xp, stream=None):
+    T, cin = X.shape
+    return _check("lcp_gather_channels", LIB.lcp_gather_channels(_p(X), T, cin, int(B), _p(perm), _p(Xp),
+                                                                 _stream(stream)))
+
+
+def lcp_sparse_gemm(vals, meta, Xp, cout, Y, stream=None):
+    T, cin = Xp.shape
+    return _check("lcp_sparse_gemm", LIB.lcp_sparse_gemm(_p(vals), _p(meta), _p(Xp), T, int(cout), cin, _p(Y),
+                                                         _stream(stream)))
+
+
+def lcp_deploy_forward(vals, meta, perm, B, X, cout, Xp, Y, stream=None):
+    T, cin = X.shape
+    return _check("lcp_deploy_forward", LIB.lcp_deploy_forward(_p(vals), _p(meta), _p(perm), int(B), _p(X), T,
+                                                               int(cout), cin, _p(Xp), _p(Y), _stream(stream)))

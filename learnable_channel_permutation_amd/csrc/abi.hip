@@ -337,6 +337,68 @@ int lcp_layer_outputs(const void* W, const void* X, lcp_dtype dt, int cout, int 
   return LCP_OK;
 }
 
+int lcp_sparse_pack_bytes(int cout, int cin, size_t* vals_bytes, size_t* meta_bytes) {
+  if (!vals_bytes || !meta_bytes || cout <= 0 || cin <= 0 || cout % 32 || cin % 32) return LCP_E_INVAL;
+  if (!fits_i32(cout, cin)) return LCP_E_INVAL;
+  *vals_bytes = sparse_vals_bytes(cout, cin);
+  *meta_bytes = sparse_meta_bytes(cout, cin);
+  return LCP_OK;
+}
+
+int lcp_sparse_pack(const void* W, int cout, int cin, int B, const int32_t* perm, const uint32_t* bits, void* vals,
+                    uint32_t* meta, void* stream) {
+  if (!W || !perm || !bits || !vals || !meta) return LCP_E_INVAL;
+  if (cout <= 0 || cin <= 0 || cout % 32 || cin % 32 || !fits_i32(cout, cin)) return LCP_E_INVAL;
+  if (!good_B(B)) return LCP_E_UNSUPPORTED;
+  if (cin % B) return LCP_E_INVAL;
+  if (!aligned16(vals) || ((uintptr_t)meta & 3u)) return LCP_E_INVAL;
+  LCP_RUN(launch_sparse_pack((const uint16_t*)W, cout, cin, B, perm, bits, (u32x4*)vals, meta, S(stream)));
+  return LCP_OK;
+}
+
+static int check_gather(const void* X, int T, int cin, int B, const int32_t* perm, const void* Xp) {
+  if (!X || !perm || !Xp || T <= 0 || cin <= 0 || !fits_i32(T, cin)) return LCP_E_INVAL;
+  if (!good_B(B)) return LCP_E_UNSUPPORTED;
+  if (cin % B) return LCP_E_INVAL;
+  if (!aligned16(Xp) || X == Xp) return LCP_E_INVAL;
+  return LCP_OK;
+}
+
+static int check_spgemm(const void* vals, const uint32_t* meta, const void* Xp, int T, int cout, int cin,
+                        const void* Y) {
+  if (!vals || !meta || !Xp || !Y || T <= 0 || cout <= 0 || cin <= 0) return LCP_E_INVAL;
+  if (cout % 32 || cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(T, cout)) return LCP_E_INVAL;
+  if (!aligned16(vals) || !aligned16(Xp) || !aligned16(Y) || ((uintptr_t)meta & 3u)) return LCP_E_INVAL;
+  return LCP_OK;
+}
+
+int lcp_gather_channels(const void* X, int T, int cin, int B, const int32_t* perm, void* Xp, void* stream) {
+  const int rc = check_gather(X, T, cin, B, perm, Xp);
+  if (rc != LCP_OK) return rc;
+  LCP_RUN(launch_gather((const uint16_t*)X, T, cin, B, perm, (uint16_t*)Xp, S(stream)));
+  return LCP_OK;
+}
+
+int lcp_sparse_gemm(const void* vals, const uint32_t* meta, const void* Xp, int T, int cout, int cin, void* Y,
+                    void* stream) {
+  const int rc = check_spgemm(vals, meta, Xp, T, cout, cin, Y);
+  if (rc != LCP_OK) return rc;
+  LCP_RUN(launch_spgemm((const u32x4*)vals, meta, (const uint16_t*)Xp, T, cout, cin, (uint16_t*)Y, S(stream)));
+  return LCP_OK;
+}
+
+int lcp_deploy_forward(const void* vals, const uint32_t* meta, const int32_t* perm, int B, const void* X, int T,
+                       int cout, int cin, void* Xp, void* Y, void* stream) {
+  int rc = check_gather(X, T, cin, B, perm, Xp);
+  if (rc != LCP_OK) return rc;
+  rc = check_spgemm(vals, meta, Xp, T, cout, cin, Y);
+  if (rc != LCP_OK) return rc;
+  if (Y == X || Y == Xp) return LCP_E_INVAL;
+  LCP_RUN(launch_gather((const uint16_t*)X, T, cin, B, perm, (uint16_t*)Xp, S(stream)));
+  LCP_RUN(launch_spgemm((const u32x4*)vals, meta, (const uint16_t*)Xp, T, cout, cin, (uint16_t*)Y, S(stream)));
+  return LCP_OK;
+}
+
 int lcp_step_workspace_bytes(int cout, int cin, int T, int B, int iters, lcp_dtype dt, size_t* bytes) {
   if (!bytes || cout <= 0 || cin <= 0 || T <= 0 || B <= 0 || iters < 1) return LCP_E_INVAL;
   if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;

@@ -124,4 +124,16 @@ hipError_t launch_adjoint_f32(const float* G, const float* W, const float* P,
                               const uint32_t* bits, int cout, int cin, int B, const AdjSplit& sp,
                               const float* ste_norms, float* part, hipStream_t s);
 
+// Deploy path (deploy.hip), bf16: packed 2:4 weights in fragment order,
+// channel gather, sparse GEMM Y[t][o] = sum_k Ws[o][k] Xp[t][k]. perm is
+// [nb][B] (entries taken mod B, B a power of two); bits row-major
+// [cout][cin/32]; cout % 32 == 0, cin % 32 == 0.
+size_t sparse_vals_bytes(int cout, int cin);
+size_t sparse_meta_bytes(int cout, int cin);
+hipError_t launch_sparse_pack(const uint16_t* W, int cout, int cin, int B, const int* perm, const uint32_t* bits,
+                              u32x4* vals, uint32_t* meta, hipStream_t s);
+hipError_t launch_gather(const uint16_t* X, int T, int cin, int B, const int* perm, uint16_t* Xp, hipStream_t s);
+hipError_t launch_spgemm(const u32x4* vals, const uint32_t* meta, const uint16_t* Xp, int T, int cout, int cin,
+                         uint16_t* Y, hipStream_t s);
+
 }  // namespace lcp
