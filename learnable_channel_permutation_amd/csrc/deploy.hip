@@ -108,15 +108,20 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
 }
 
 // ---- 2:4 sparse GEMM ----------------------------------------------------------------
-// Y[t][o] = sum_k Ws[o][k] Xp[t][k]. 256 (rows o) x 128 (tokens t) tiles, K step
-// 64, 8 waves in a 4 x 2 layout (each wave 64 x 64: 2 x 2 sparse MFMA
-// blocks). Per stage: the 16 weight fragments of the tile (16 KB, lane
-// order, linear LDS reads), their position words (2 KB) and the 128 x 64
-// activation tile (16 KB, rows swizzled as in the dense GEMM), all moved with
-// direct-to-LDS loads into a three-stage ring; one barrier per K step.
-constexpr int SP_BM = 256, SP_BN = 128, SP_S = 3, SP_NT = 512;
-constexpr int SP_A = (SP_BM / 32) * 2 * 1024, SP_M = (SP_BM / 32) * 256, SP_B = SP_BN * 64 * 2;
-constexpr int SP_STAGE = SP_A + SP_M + SP_B;
+// Y[t][o] = sum_k Ws[o][k] Xp[t][k]. 256 (rows o) x 128 (tokens t) tiles, 128
+// positions of K per stage, 8 waves in a 4 x 2 layout (each wave 64 x 64: 2 x 2
+// sparse MFMA blocks). A stage holds the 32 weight fragments of the tile
+// (32 KB, lane order, linear LDS reads), their position words (4 KB) and two
+// 128 x 64 activation sub-tiles (32 KB, rows swizzled as in the dense GEMM),
+// all moved with direct-to-LDS loads; two stages, one barrier per stage. The
+// kernel is bound by the rate at which a CU can pull tiles from L2 into LDS
+// (about 20 bytes per clock): 256 x 128 tiles minimise the bytes per useful
+// flop for one tile per CU, and 128 positions per stage halve the barriers of
+// a 64-position step.
+constexpr int SP_BM = 256, SP_BN = 128, SP_S = 2, SP_KK = 2, SP_NT = 512;
+constexpr int SP_A1 = (SP_BM / 32) * 2 * 1024, SP_M1 = (SP_BM / 32) * 256, SP_B1 = SP_BN * 64 * 2;
+constexpr int SP_STAGE = SP_KK * (SP_A1 + SP_M1 + SP_B1);
+constexpr int SP_MOFF = SP_KK * SP_A1, SP_BOFF = SP_KK * (SP_A1 + SP_M1);
 
 __device__ __forceinline__ void sp_tile_coords(int g, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
   // consecutive workgroups of one XCD (id mod 8) take a compact group of
@@ -134,16 +139,11 @@ __device__ __forceinline__ void sp_tile_coords(int g, int G, int tiles_m, int ti
 
 __device__ __forceinline__ int sp_swz(int row, int ch) { return row * 64 + ((ch ^ ((row >> 1) & 7)) << 3); }
 
-template <int N>
-__device__ __forceinline__ void sp_wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restrict__ vals,
                                                           const uint32_t* __restrict__ meta,
                                                           const uint16_t* __restrict__ Xp, int T, int cout,
                                                           int cin, uint16_t* __restrict__ Y) {
-  constexpr int FM = 2, FN = 2, WM = 64, WN = 64;
+  constexpr int FM = 2, FN = 2, WM = 64, WN = 64, KK = SP_KK;
   extern __shared__ __attribute__((aligned(16))) unsigned char sp_lds[];
   const int tiles_m = (cout + SP_BM - 1) / SP_BM, tiles_n = (T + SP_BN - 1) / SP_BN;
   int tm, tn;
@@ -153,28 +153,36 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
   const int wm = w >> 1, wn = w & 1;
   const int h = l >> 5, ln = l & 31;
   const int KF = cin / 32, KT = (cin + 63) / 64, RG = cout / 32;
+  const int NKS = (cin + 64 * KK - 1) / (64 * KK);
 
-  auto issue = [&](int stage, int kt) {
+  // stage ks: weight fragments f = rgl * 2KK + kh (row group rgl, 32-position
+  // fragment kh of the stage), position words [rgl][kk], activation sub-tile kk
+  auto issue = [&](int stage, int ks) {
     unsigned char* sb = sp_lds + stage * SP_STAGE;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {                       // weight fragments f = 8q + w
-      const int f = 8 * q + w, rg = m0 / 32 + (f >> 1), kf = 2 * kt + (f & 1);
+    for (int q = 0; q < 2 * KK; ++q) {
+      const int f = 8 * q + w, rgl = f / (2 * KK), kh = f % (2 * KK);
+      const int rg = m0 / 32 + rgl, kf = ks * 2 * KK + kh;
       const void* src = (rg < RG && kf < KF) ? (const void*)(vals + ((size_t)rg * KF + kf) * 64 + l)
                                              : (const void*)g_dep_zero;
       __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + f * 1024), 16, 0, 0);
     }
-    {                                                   // position words of row group w
-      const int rg = m0 / 32 + w;
-      const void* src = (rg < RG) ? (const void*)(meta + ((size_t)rg * KT + kt) * 64 + l) : (const void*)g_dep_zero;
-      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_A + w * 256), 4, 0, 0);
+#pragma unroll
+    for (int q = 0; q < KK; ++q) {
+      const int rg = m0 / 32 + w, kd = ks * KK + q;
+      const void* src = (rg < RG && kd < KT) ? (const void*)(meta + ((size_t)rg * KT + kd) * 64 + l)
+                                             : (const void*)g_dep_zero;
+      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_MOFF + (w * KK + q) * 256), 4, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {                       // activation rows
-      const int c = (q * 8 + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
-      const int gn = n0 + row, gk = kt * 64 + ch * 8;
-      const void* src = (gn < T && gk < cin) ? (const void*)(Xp + (size_t)gn * cin + gk) : (const void*)g_dep_zero;
-      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_A + SP_M + (q * 8 + w) * 1024), 16, 0, 0);
-    }
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = (q * 8 + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+        const int gn = n0 + row, gk = (ks * KK + kk) * 64 + ch * 8;
+        const void* src = (gn < T && gk < cin) ? (const void*)(Xp + (size_t)gn * cin + gk) : (const void*)g_dep_zero;
+        __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_BOFF + kk * SP_B1 + (q * 8 + w) * 1024), 16, 0, 0);
+      }
   };
 
   floatx16 acc[FM][FN];
@@ -186,47 +194,47 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
   auto compute = [&](int stage) {
     const unsigned char* sb = sp_lds + stage * SP_STAGE;
     const u32x4* LA = reinterpret_cast<const u32x4*>(sb);
-    const uint32_t* LM = reinterpret_cast<const uint32_t*>(sb + SP_A);
-    const uint16_t* LB = reinterpret_cast<const uint16_t*>(sb + SP_A + SP_M);
-    uint32_t mw[FM];
+    const uint32_t* LM = reinterpret_cast<const uint32_t*>(sb + SP_MOFF);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) mw[i] = LM[(wm * FM + i) * 64 + l];
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint16_t* LB = reinterpret_cast<const uint16_t*>(sb + SP_BOFF + kk * SP_B1);
+      uint32_t mw[FM];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      u32x4 a[FM];
-      bf16x16 bv[FN];
+      for (int i = 0; i < FM; ++i) mw[i] = LM[((wm * FM + i) * KK + kk) * 64 + l];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = LA[((wm * FM + i) * 2 + p) * 64 + l];
+      for (int p = 0; p < 2; ++p) {
+        u32x4 a[FM];
+        bf16x16 bv[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * WN + 32 * j + ln;
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + h)]);
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + 2 + h)]);
-        typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-        const u32x8 bb = u32x8{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        bv[j] = __builtin_bit_cast(bf16x16, bb);
-      }
+        for (int i = 0; i < FM; ++i) a[i] = LA[((wm * FM + i) * 2 * KK + 2 * kk + p) * 64 + l];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int idx = (int)((mw[i] >> (16 * p)) & 0xffffu);
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * WN + 32 * j + ln;
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + h)]);
+          const u32x4 b1 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + 2 + h)]);
+          typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+          bv[j] = __builtin_bit_cast(bf16x16, u32x8{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w});
+        }
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(a[i]), bv[j], acc[i][j], idx, 0, 0);
+        for (int i = 0; i < FM; ++i) {
+          const int idx = (int)((mw[i] >> (16 * p)) & 0xffffu);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(a[i]), bv[j], acc[i][j], idx, 0, 0);
+        }
       }
     }
   };
 
-  // ring as in the dense GEMM: tiles kt + 1 .. kt + S - 2 in flight while kt
-  // is multiplied; the barrier also retires the reads of the stage refilled next
-  constexpr int NL = 5;                                 // load instructions per tile per thread
-  for (int q = 0; q < SP_S - 1; ++q)
-    if (q < KT) issue(q, q);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) sp_wait_vmcnt<NL>();
-    else sp_wait_vmcnt<0>();
+  // two stages: stage ks + 1 is loaded while stage ks is multiplied; the
+  // wait retires this thread's loads of stage ks, the barrier everyone's, and
+  // also the reads of the stage that is refilled next
+  if (NKS > 0) issue(0, 0);
+  for (int ks = 0; ks < NKS; ++ks) {
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __builtin_amdgcn_s_barrier();
-    if (kt + SP_S - 1 < KT) issue((kt + SP_S - 1) % SP_S, kt + SP_S - 1);
-    compute(kt % SP_S);
+    if (ks + 1 < NKS) issue((ks + 1) & 1, ks + 1);
+    compute(ks & 1);
   }
 
   // lane (h, ln) of block (i, j): token n0 + wn*64 + 32j + ln, rows
