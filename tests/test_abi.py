@@ -171,3 +171,37 @@ def test_step_argument_validation():
     assert lib.lcp_layer_outputs(p, p, L.LCP_BF16, 8, 48, 16, p, p, p, en, s) == L.LCP_E_INVAL
     assert lib.lcp_layer_outputs(p, p, 9, 8, 64, 16, p, p, p, en, s) == L.LCP_E_UNSUPPORTED
     assert lib.lcp_layer_outputs(p, p, L.LCP_BF16, 8, 64, 16, p, p, p, ctypes.c_size_t(16), s) == L.LCP_E_WORKSPACE
+
+
+def test_deploy_argument_validation():
+    """Deploy entry points reject bad sizes, block sizes and alignment before
+    any launch (no GPU needed: nothing is enqueued on an error)."""
+    L = _lib()
+    lib = L.LIB
+    p = 0x100000
+    s = None
+    vb, mb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.lcp_sparse_pack_bytes(4096, 11008, ctypes.byref(vb), ctypes.byref(mb)) == L.LCP_OK
+    assert vb.value == 4096 * 11008 and mb.value == (4096 // 32) * ((11008 + 63) // 64) * 64 * 4
+    assert lib.lcp_sparse_pack_bytes(100, 64, ctypes.byref(vb), ctypes.byref(mb)) == L.LCP_E_INVAL
+    assert lib.lcp_sparse_pack_bytes(64, 48, ctypes.byref(vb), ctypes.byref(mb)) == L.LCP_E_INVAL
+    # pack
+    assert lib.lcp_sparse_pack(None, 64, 128, 64, p, p, p, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_sparse_pack(p, 60, 128, 64, p, p, p, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_sparse_pack(p, 64, 128, 48, p, p, p, p, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_sparse_pack(p, 64, 96, 64, p, p, p, p, s) == L.LCP_E_INVAL       # cin % B
+    assert lib.lcp_sparse_pack(p, 64, 128, 64, p, p, p + 8, p, s) == L.LCP_E_INVAL   # vals alignment
+    assert lib.lcp_sparse_pack(p, 64, 128, 64, p, p, p, p + 2, s) == L.LCP_E_INVAL   # meta alignment
+    # gather
+    assert lib.lcp_gather_channels(p, 0, 128, 64, p, p + 4096, s) == L.LCP_E_INVAL
+    assert lib.lcp_gather_channels(p, 8, 128, 96, p, p + 4096, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_gather_channels(p, 8, 128, 64, p, p, s) == L.LCP_E_INVAL            # in place
+    assert lib.lcp_gather_channels(p, 8, 128, 64, p, p + 8, s) == L.LCP_E_INVAL        # alignment
+    # sparse GEMM and the combined call
+    assert lib.lcp_sparse_gemm(p, p, p, 8, 60, 128, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_sparse_gemm(p, p, p, 8, 64, 80, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_sparse_gemm(p, p + 2, p, 8, 64, 128, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_sparse_gemm(p, p, p, 8, 64, 128, p + 8, s) == L.LCP_E_INVAL
+    assert lib.lcp_deploy_forward(p, p, p, 64, p, 8, 64, 128, p + 4096, p, s) == L.LCP_E_INVAL   # Y aliases X
+    assert lib.lcp_deploy_forward(p, p, p, 64, p, 8, 64, 128, p, p + 4096, s) == L.LCP_E_INVAL   # Xp aliases X
+    assert lib.lcp_deploy_forward(p, p, p, 32, p, 8, 60, 128, p + 4096, p + 8192, s) == L.LCP_E_INVAL
