@@ -63,10 +63,22 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+# source files each timed kernel is built from (with the shared common.h):
+# its HBM counters stay valid until one of them changes
+KERNEL_SOURCES = {
+    "layer_init": ["layer.hip"], "sinkhorn_fwd": ["sinkhorn.hip", "frag.h"],
+    "sinkhorn_bwd": ["sinkhorn.hip"], "permute_mask_unpermute": ["permute.hip", "frag.h"],
+    "error_gemm": ["gemm.hip"], "dD_gemm": ["gemm.hip"], "error_finalize": ["gemm.hip"],
+    "block_adjoint": ["adjoint.hip"], "harden": ["harden.hip", "frag.h"],
+    "cosine_finalize": ["cosine.hip"], "cosine_grad": ["cosine.hip"],
+    "sparse_gemm": ["deploy.hip"], "gather": ["deploy.hip"], "sparse_pack": ["deploy.hip"],
+}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "learnable_channel_permutation_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ["common.h"] + sorted(KERNEL_SOURCES.get(kernel, [])):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -74,16 +86,16 @@ def kernel_source_hash():
 
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the kernel's current sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
     k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    if k is None or kernel not in KERNEL_SOURCES or k.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return k.get("bytes_per_launch")
 
 
 class HipEvents:
