@@ -84,9 +84,10 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, shape):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the kernel's current sources; else None."""
+    was taken on the kernel's current sources and on this layer shape
+    ([cout, cin, T]); else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -94,6 +95,8 @@ def measured_traffic(kernel):
         return None
     k = t.get("kernels", {}).get(kernel)
     if k is None or kernel not in KERNEL_SOURCES or k.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    if list(k.get("shape", [])) != list(shape):
         return None
     return k.get("bytes_per_launch")
 
@@ -268,7 +271,7 @@ def run_deploy(args, torch, lcp, lcp_synth):
         "config": {"workload": "lcp_deploy_forward", "layer": spec.name, "cout": cout, "cin": cin, "T": T,
                    "B": B, "N": 2, "M": 4},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("sparse_gemm"),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("sparse_gemm", [cout, cin, T]),
                      "kernel": "sparse_gemm", "kernel_ms": round(s_ms, 4),
                      "note": "flops = nonzero multiply-adds x 2, priced against the dense bf16 peak"},
         "gather": {"ms": round(g_ms, 4), "GB/s": round(gather_bytes / (g_ms * 1e-3) / 1e9, 1)},
@@ -398,7 +401,7 @@ def main():
     if bwd_gemm_ms > fwd_gemm_ms:
         dom_name, dom_ms = ("dD_gemm", bwd_gemm_ms)
     achieved = flops_gemm / (dom_ms * 1e-3) / 1e12
-    traffic = measured_traffic(dom_name)
+    traffic = measured_traffic(dom_name, [spec.cout, spec.cin, spec.T])
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
             "kernel_ms": round(dom_ms, 4),

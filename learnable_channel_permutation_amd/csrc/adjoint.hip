@@ -27,10 +27,11 @@
 // which is S_b^T ((G_b P_b) . (W_b P_b)): the gradient reaching the 0/1 mask,
 // dE/dM = (G_b P_b) . W_hat_b, handed unchanged to S_hat_b = S_b P_b.
 // For B = 128 the four waves of a workgroup take the same 32-row tile, share
-// one ring (each wave issues a quarter of the loads, a barrier per tile) and
-// each owns one 32-wide column block of dP (register budget); for B <= 64
+// one four-stage ring (each wave issues a quarter of the loads, a barrier per
+// tile) and each owns one 32-wide block of positions k: it forms W_hat and Y
+// for its own positions only and transposes all of G and W; for B <= 64
 // every wave owns whole tiles and its own ring. Partial sums of waves owning
-// the same columns are added through LDS in a fixed order.
+// the same entries are added through LDS in a fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -44,15 +45,31 @@ struct AdjGeom {
   static constexpr int KS = B / 16;             // K steps over a block
   static constexpr int TT = B / 32;             // 32-wide column blocks
   static constexpr int WS = (B == 128) ? 4 : 1; // waves sharing one row tile
-  static constexpr int OWN = TT / WS;           // column blocks (t2) owned per wave
+  static constexpr int NA = TT / WS;            // position blocks (a) owned per wave
   static constexpr int TILES = 4 / WS;          // row tiles in flight per workgroup
   static constexpr int ROWS = 32 * TILES;       // rows per workgroup step
   static constexpr int FRAG = TT * KS * 64;     // u32x4 entries of the P fragments
-  static constexpr int S = 2;                   // ring stages per wave
+  // ring stages: B = 128 keeps one row tile per workgroup, so a deeper ring
+  // gives the CU enough bytes in flight to stream at HBM rate
+  static constexpr int S = (B == 128) ? 4 : 2;
   static constexpr int BI = (TT + 1) / 2;       // mask-word load instructions per tile
   static constexpr int STAGE = 2 * KS * 1024 + BI * 256;   // bytes per stage
   static constexpr int IPT = 2 * KS + BI;       // load instructions per tile
 };
+
+// s_waitcnt vmcnt(n) for the wave-uniform counts the ring can need
+// (0 and up to two later tiles of 4 or 5 loads); any other count waits for
+// everything, which is always safe.
+__device__ __forceinline__ void adj_wait_vm(int n) {
+  constexpr int E = (7 << 4) | (15 << 8);
+  switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(4 | E); break;
+    case 5: __builtin_amdgcn_s_waitcnt(5 | E); break;
+    case 8: __builtin_amdgcn_s_waitcnt(8 | E); break;
+    case 10: __builtin_amdgcn_s_waitcnt(10 | E); break;
+    default: __builtin_amdgcn_s_waitcnt(0 | E); break;
+  }
+}
 
 __device__ __forceinline__ u32x4 identity_slots(int v, int h, int n) {
   // MFMA B operand of the 32 x 32 identity, K step v: slot e of lane (h, n)
@@ -76,7 +93,7 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
     const float* __restrict__ P, const uint32_t* __restrict__ bits, int cout, int cin, int tpw,
     int maxseg, const float* __restrict__ ste_norms, float* __restrict__ part) {
   using Gm = AdjGeom<B>;
-  constexpr int KS = Gm::KS, TT = Gm::TT, WS = Gm::WS, OWN = Gm::OWN, TILES = Gm::TILES;
+  constexpr int KS = Gm::KS, TT = Gm::TT, WS = Gm::WS, NA = Gm::NA, TILES = Gm::TILES;
   constexpr int S = Gm::S, STAGE = Gm::STAGE;
   extern __shared__ __attribute__((aligned(16))) unsigned char adj_lds[];
   // layout: P fragments | rings (one per row-tile slot, S stages); after the
@@ -88,7 +105,7 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int h = l >> 5, n = l & 31;
   const int slot = w / WS;          // row tile slot of this wave
-  const int half = w % WS;          // column blocks t2 = half * OWN + o
+  const int half = w % WS;          // position blocks a = half * NA + ai
   unsigned char* ring = rings + slot * S * STAGE;
   const u32x4* F = reinterpret_cast<const u32x4*>(fb);
   const int lrow = remap_row(n);    // tile row whose operands this lane fetches
@@ -119,15 +136,15 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
     }
     __syncthreads();
 
-    floatx16 acc[TT][OWN];
+    floatx16 acc[NA][TT];
 #pragma unroll
-    for (int a = 0; a < TT; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int o = 0; o < OWN; ++o) acc[a][o] = floatx16{};
-    // column norms n_j of this lane's source channels j = bB + 32 t2 + n
-    float nrm[OWN];
+      for (int o = 0; o < TT; ++o) acc[a][o] = floatx16{};
+    // column norms n_j of this lane's source channels j = bB + 32 o + n
+    float nrm[TT];
 #pragma unroll
-    for (int o = 0; o < OWN; ++o) nrm[o] = STE ? ste_norms[b * B + 32 * (half * OWN + o) + n] : 0.f;
+    for (int o = 0; o < TT; ++o) nrm[o] = STE ? ste_norms[b * B + 32 * o + n] : 0.f;
 
     // the load instructions of one tile into stage st (with WS waves sharing a
     // ring, wave `half` issues every WS-th of them)
@@ -137,7 +154,7 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
       const int i = i0 + lrow;
 #pragma unroll
       for (int p = 0; p < KS; ++p) {
-        if ((2 * p) % WS != half) continue;
+        if (p % WS != half) continue;
         const size_t o = (size_t)i * cin + b * B + 16 * p + 8 * h;
         const void* sw = (i < cout) ? (const void*)(W + o) : (const void*)g_adj_zero;
         const void* sg = (i < cout) ? (const void*)(G + o) : (const void*)g_adj_zero;
@@ -159,26 +176,32 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
 
     const int first = seg + slot;
     const int ntile = (first < seg_end) ? (seg_end - first + TILES - 1) / TILES : 0;
-    if (ntile > 0) issue(0, first);
+    // loads this wave issues per tile (the waves of a shared ring split them)
+    const int nload = 2 * (KS / WS) + (WS == 1 ? Gm::BI : (half < Gm::BI ? 1 : 0));
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q)
+      if (q < ntile) issue(q, first + q * TILES);
     for (int it = 0; it < ntile; ++it) {
-      // this wave's loads of tile `it` have landed (nothing later is in flight);
-      // the other stage was consumed in the previous iteration and is refilled.
-      // A shared ring also needs every wave's part and every wave done with the
-      // other stage: one barrier.
-      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+      // this wave's loads of tile `it` have landed (only later tiles' loads,
+      // issued after them, may still be in flight); the stage refilled below
+      // was consumed in the previous iteration. A shared ring also needs every
+      // wave's part and every wave done with that stage: one barrier.
+      const int later = min(S - 2, ntile - 1 - it);
+      if (S == 2) __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+      else adj_wait_vm(later * nload);
       if (WS > 1) __builtin_amdgcn_s_barrier();
-      if (it + 1 < ntile) issue((it + 1) & 1, first + (it + 1) * TILES);
-      const unsigned char* sb = ring + (it & 1) * STAGE;
+      if (it + S - 1 < ntile) issue((it + S - 1) % S, first + (it + S - 1) * TILES);
+      const unsigned char* sb = ring + (it % S) * STAGE;
       const u32x4* LW = reinterpret_cast<const u32x4*>(sb);
       const u32x4* LG = reinterpret_cast<const u32x4*>(sb + KS * 1024);
       const uint32_t* LB = reinterpret_cast<const uint32_t*>(sb + 2 * KS * 1024);
 
-      // transposed G and W (and S = |W| n_j) for the owned column blocks:
-      // 16 rows per lane
-      u32x4 gT[OWN][2], wT[OWN][2], sT[OWN][2];
+      // transposed G and W (and S = |W| n_j) for all column blocks of the
+      // source channels j: 16 rows per lane
+      u32x4 gT[TT][2], wT[TT][2], sT[TT][2];
 #pragma unroll
-      for (int o = 0; o < OWN; ++o) {
-        const int t2 = half * OWN + o;
+      for (int o = 0; o < TT; ++o) {
+        const int t2 = o;
         floatx16 tg = {}, tw = {};
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
@@ -201,7 +224,8 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
         }
       }
 #pragma unroll
-      for (int a = 0; a < TT; ++a) {
+      for (int ai = 0; ai < NA; ++ai) {
+        const int a = half * NA + ai;
         // W_hat and Y for positions 32a + n, rows 16h + r
         floatx16 wh = {}, yy = {};
 #pragma unroll
@@ -232,11 +256,11 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
           yop[u] = u32x4{pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]), pack2(yv[6], yv[7])};
         }
 #pragma unroll
-        for (int o = 0; o < OWN; ++o)
+        for (int o = 0; o < TT; ++o)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            acc[a][o] = mfma32(aop[u], gT[o][u], acc[a][o]);
-            acc[a][o] = mfma32(yop[u], wT[o][u], acc[a][o]);
+            acc[ai][o] = mfma32(aop[u], gT[o][u], acc[ai][o]);
+            acc[ai][o] = mfma32(yop[u], wT[o][u], acc[ai][o]);
           }
         if (STE) {
           // (W_hat . Y), unmasked
@@ -249,49 +273,50 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
             qop[u] = u32x4{pack2(qv[0], qv[1]), pack2(qv[2], qv[3]), pack2(qv[4], qv[5]), pack2(qv[6], qv[7])};
           }
 #pragma unroll
-          for (int o = 0; o < OWN; ++o)
+          for (int o = 0; o < TT; ++o)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) acc[a][o] = mfma32(qop[u], sT[o][u], acc[a][o]);
+            for (int u = 0; u < 2; ++u) acc[ai][o] = mfma32(qop[u], sT[o][u], acc[ai][o]);
         }
       }
     }
 
-    // lane (h, n) of block (a, o) holds dP^T[k = 32a + 8(r/4) + 4h + r%4][j = 32 t2 + n];
-    // waves owning the same t2 are added into slot 0, one slot per round
+    // lane (h, n) of block (ai, o) holds dP^T[k = 32a + 8(r/4) + 4h + r%4][j = 32 o + n]
+    // with a = half * NA + ai; the row-tile slots are added into slot 0, one
+    // slot per round
     if (TILES > 1) {
       for (int s2 = 1; s2 < TILES; ++s2) {
         __syncthreads();
         if (slot == s2) {
 #pragma unroll
-          for (int a = 0; a < TT; ++a)
+          for (int a = 0; a < NA; ++a)
 #pragma unroll
-            for (int o = 0; o < OWN; ++o)
+            for (int o = 0; o < TT; ++o)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l] = acc[a][o][r];
+              for (int r = 0; r < 16; ++r) red[(((half * NA + a) * TT + o) * 16 + r) * 64 + l] = acc[a][o][r];
         }
         __syncthreads();
         if (slot == 0) {
 #pragma unroll
-          for (int a = 0; a < TT; ++a)
+          for (int a = 0; a < NA; ++a)
 #pragma unroll
-            for (int o = 0; o < OWN; ++o)
+            for (int o = 0; o < TT; ++o)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[a][o][r] += red[(((half * TT + a) * OWN + o) * 16 + r) * 64 + l];
+              for (int r = 0; r < 16; ++r) acc[a][o][r] += red[(((half * NA + a) * TT + o) * 16 + r) * 64 + l];
         }
       }
     }
     if (slot == 0) {
       float* dst = part + ((size_t)blockIdx.x * maxseg + (b - first_b)) * B * B;
 #pragma unroll
-      for (int a = 0; a < TT; ++a)
+      for (int ai = 0; ai < NA; ++ai)
 #pragma unroll
-        for (int o = 0; o < OWN; ++o) {
-          const int j = 32 * (half * OWN + o) + n;
+        for (int o = 0; o < TT; ++o) {
+          const int j = 32 * o + n;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int k = 32 * a + 8 * q + 4 * h;
+            const int k = 32 * (half * NA + ai) + 8 * q + 4 * h;
             *reinterpret_cast<floatx4*>(dst + j * B + k) =
-                floatx4{acc[a][o][4 * q], acc[a][o][4 * q + 1], acc[a][o][4 * q + 2], acc[a][o][4 * q + 3]};
+                floatx4{acc[ai][o][4 * q], acc[ai][o][4 * q + 1], acc[ai][o][4 * q + 2], acc[ai][o][4 * q + 3]};
           }
         }
     }
@@ -303,7 +328,7 @@ template <int B>
 constexpr size_t adj_lds_bytes() {
   using Gm = AdjGeom<B>;
   const size_t ring = (size_t)Gm::TILES * Gm::S * Gm::STAGE;
-  const size_t red = Gm::TILES > 1 ? (size_t)Gm::WS * Gm::TT * Gm::OWN * 16 * 64 * 4 : 0;
+  const size_t red = Gm::TILES > 1 ? (size_t)Gm::WS * Gm::NA * Gm::TT * 16 * 64 * 4 : 0;
   return (size_t)Gm::FRAG * 16 + (ring > red ? ring : red);
 }
 
