@@ -148,40 +148,48 @@ class _Ev:
         self.cuda_event = h.value
 
 
-def cpu_baseline(spec, lay, hard=False, loss="frobenius", mask_ste=False):
-    """The float64 oracle, untuned, for one full forward + backward step of the
-    same layer on the host cores (one step is the sample)."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
-    t0 = time.perf_counter()
-    fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M, hard=hard,
-                             loss=loss)
-    if spec.backward:
-        oracle.step_backward(fw, lay.X, lay.W, mask_ste=mask_ste)
-    dt = time.perf_counter() - t0
-    return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": "one full %s step of the same %dx%d layer (T=%d), float64 NumPy, %.1f s"
-                      % ("forward+backward" if spec.backward else "forward", spec.cout, spec.cin, spec.T, dt)}
+        return os.cpu_count()
+
+
+def cpu_baseline(spec, lay, hard=False, loss="frobenius", mask_ste=False):
+    """The float64 oracle, untuned, for full forward + backward steps of the
+    same layer on the host cores: the median of 3 steps (1 for layers above
+    10^8 weights)."""
+    import oracle
+    reps = 3 if spec.cout * spec.cin <= 10 ** 8 else 1
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M, hard=hard,
+                                 loss=loss)
+        if spec.backward:
+            oracle.step_backward(fw, lay.X, lay.W, mask_ste=mask_ste)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(_blas_threads()), "cpu_count": os.cpu_count(),
+            "kind": "oracle",
+            "sample": "median of %d full %s steps of the same %dx%d layer (T=%d), float64 NumPy, %.1f s each"
+                      % (reps, "forward+backward" if spec.backward else "forward", spec.cout, spec.cin, spec.T, dt)}
 
 
 def cpu_baseline_deploy(W, X, P, mask):
-    """The float64 oracle's deployed-layer forward on the host cores (one
-    full forward of the same layer is the sample)."""
+    """The float64 oracle's deployed-layer forward on the host cores: the
+    median of 5 full forwards of the same layer."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
-    t0 = time.perf_counter()
-    oracle.deploy_forward(W, X, P, mask)
-    dt = time.perf_counter() - t0
-    return {"value": 1.0 / dt, "unit": "forwards/s", "cores": int(cores), "kind": "oracle",
-            "sample": "one full deployed-layer forward (%dx%d weight, %d tokens), float64 NumPy, %.1f s"
+    times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        oracle.deploy_forward(W, X, P, mask)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": 1.0 / dt, "unit": "forwards/s", "cores": int(_blas_threads()), "cpu_count": os.cpu_count(),
+            "kind": "oracle",
+            "sample": "median of 5 full deployed-layer forwards (%dx%d weight, %d tokens), float64 NumPy, %.2f s each"
                       % (W.shape[0], W.shape[1], X.shape[0], dt)}
 
 
@@ -230,6 +238,7 @@ def run_deploy(args, torch, lcp, lcp_synth):
     ms = t_start.elapsed_time(t_stop) / K
     g_ms = sum(he.ms(a, b) for a, b, _ in ev) / K
     s_ms = sum(he.ms(b, c) for _, b, c in ev) / K
+    ms_median = float(np.median([he.ms(a, c) for a, _, c in ev]))
     he.close()
     # context on the same box: PyTorch's own gather and dense bf16 GEMM
     gidx = torch.from_numpy((np.arange(nb)[:, None] * B + perm_np).reshape(-1).astype(np.int64)).to(dev)
@@ -266,6 +275,7 @@ def run_deploy(args, torch, lcp, lcp_synth):
         "value": round(1000.0 / ms, 2),
         "unit": "forwards/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_median, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded LLaMA-shaped layer, random block permutation and 2:4 mask)",
         "config": {"workload": "lcp_deploy_forward", "layer": spec.name, "cout": cout, "cin": cin, "T": T,
@@ -386,13 +396,17 @@ def main():
     tfs = [lcp.make_timing([None, None, _Ev(a)], [None, None, _Ev(b)]) for a, b in g_fwd]
     tbs = [lcp.make_timing([_Ev(a)], [_Ev(b)]) for a, b in g_bwd]
     t_start, t_stop = ev(), ev()
+    bounds = [ev() for _ in range(K + 1)]
     torch.cuda.synchronize()
     t_start.record(stream)
+    bounds[0].record(stream)
     for k in range(K):
         step(tfs[k], tbs[k] if spec.backward else None)
+        bounds[k + 1].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_stop) / K
+    ms_median = float(np.median([bounds[k].elapsed_time(bounds[k + 1]) for k in range(K)]))
     fwd_gemm_ms = sum(he.ms(a, b) for a, b in g_fwd) / K
     bwd_gemm_ms = sum(he.ms(a, b) for a, b in g_bwd) / K if spec.backward else 0.0
 
@@ -450,6 +464,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_median, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
