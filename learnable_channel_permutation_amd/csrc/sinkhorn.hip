@@ -11,8 +11,10 @@
 // (a < 4) and columns lc*CPL + c (c < CPL = B/16), all in registers for every
 // iteration (no HBM or LDS round trip of the block). Row reductions run over
 // the 16 lanes of a DPP row; column reductions pair lanes 16 and 32 apart
-// (permlane swaps) and then combine the waves' (max, sum) pairs through LDS
-// with one barrier per column step. Work is done in base 2:
+// (permlane swaps), then the waves' (max, sum) pairs meet in LDS: wave w
+// merges the pairs of columns 16w .. 16w+15 (four lanes per column, each
+// taking every fourth wave, merged across lanes 16 and 32 apart) and
+// publishes the column offsets, two barriers per column step. Work is done in base 2:
 // z = logits * log2(e) / tau, lse2 = max + log2(sum exp2(z - max)), so each
 // normalisation costs one v_exp_f32 per element. The row offsets r_i and
 // column offsets c_i (base 2) are kept for the reverse pass.
@@ -65,13 +67,34 @@ __device__ __forceinline__ void ld_block(const float* __restrict__ src, float (&
   for (int a = 0; a < 4; ++a) ld_cols<CPL>(src + (16 * w + 4 * lr + a) * B + lc * CPL, v[a]);
 }
 
+// Value of the lane 16 (or 32) apart, from the permlane swaps (the swap
+// returns the pair in lane order, so the partner is the other element).
+__device__ __forceinline__ float partner16(float v, int l) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((l & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float partner32(float v, int l) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((l & 32) ? r[0] : r[1]);
+}
+// (m, s) <- the (max, sum of exp2(x - max)) pair of the union of two sets;
+// an empty set is (-inf, 0). Symmetric in its operands, bit for bit.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  const float a = (s > 0.f) ? s * exp2_(m - mn) : 0.f;
+  const float b = (s2 > 0.f) ? s2 * exp2_(m2 - mn) : 0.f;
+  m = mn;
+  s = a + b;
+}
+
 // One forward iteration on the register block, using reduction buffer `red`
-// (WAVES * B (max, sum) pairs; alternate two buffers between iterations).
+// (WAVES * B (max, sum) pairs; alternate two buffers between iterations) and
+// `ccb` (B column offsets).
 // Writes the row offsets of this lane's rows to roff[row] (if lc == 0) and the
 // column offsets to coff[col] (if w == 0 && lr == 0); either may be null.
 template <int B>
-__device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* red, float* roff, float* coff,
-                                        int w, int lr, int lc) {
+__device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* red, float* ccb, float* roff,
+                                        float* coff, int w, int lr, int lc) {
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
   // ---- row step: U = Z - lse_row(Z)
@@ -100,22 +123,28 @@ __device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* r
     if (lr == 0) red[w * B + lc * CPL + c] = float2{m, s};
   }
   __syncthreads();
+  // wave w merges columns 16w + lc over the waves: quarter lr takes waves
+  // lr, lr + 4, ..., then the quarters meet across lanes 16 and 32 apart
+  {
+    const int l = 16 * lr + lc, col = 16 * w + lc;
+    float m = -__builtin_inff(), s = 0.f;
+#pragma unroll
+    for (int v = lr; v < WAVES; v += 4) {
+      const float2 pv = red[v * B + col];
+      lse_merge(m, s, pv.x, pv.y);
+    }
+    lse_merge(m, s, partner16(m, l), partner16(s, l));
+    lse_merge(m, s, partner32(m, l), partner32(s, l));
+    if (lr == 0) ccb[col] = m + log2_(s);
+  }
+  __syncthreads();
+  float cv[CPL];
+  ld_cols<CPL>(ccb + lc * CPL, cv);
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int col = lc * CPL + c;
-    float2 pv[WAVES];
 #pragma unroll
-    for (int v = 0; v < WAVES; ++v) pv[v] = red[v * B + col];
-    float m = pv[0].x;
-#pragma unroll
-    for (int v = 1; v < WAVES; ++v) m = fmaxf(m, pv[v].x);
-    float s = 0.f;
-#pragma unroll
-    for (int v = 0; v < WAVES; ++v) s += pv[v].y * exp2_(pv[v].x - m);
-    const float cc = m + log2_(s);
-#pragma unroll
-    for (int a = 0; a < 4; ++a) z[a][c] -= cc;
-    if (coff != nullptr && w == 0 && lr == 0) coff[col] = cc;
+    for (int a = 0; a < 4; ++a) z[a][c] -= cv[c];
+    if (coff != nullptr && w == 0 && lr == 0) coff[lc * CPL + c] = cv[c];
   }
 }
 
@@ -130,6 +159,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
   constexpr int WAVES = SkGeom<B>::WAVES;
   constexpr int PP = B + 2;                       // LDS row pitch of the staged block
   __shared__ float2 red[2][WAVES * B];
+  __shared__ __attribute__((aligned(16))) float ccb[B];
   extern __shared__ float ps[];                   // [B][PP] P block, then [B] norms
   const int b = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l >> 4, lc = l & 15;
@@ -142,7 +172,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
   for (int it = 0; it < iters; ++it) {
     float* ro = off ? off + ((size_t)(b * iters + it) * 2 + 0) * B : nullptr;
     float* co = off ? off + ((size_t)(b * iters + it) * 2 + 1) * B : nullptr;
-    sk_iter<B>(z, red[it & 1], ro, co, w, lr, lc);
+    sk_iter<B>(z, red[it & 1], ccb, ro, co, w, lr, lc);
   }
   float* dst = P + (size_t)b * B * B;
 #pragma unroll
@@ -187,6 +217,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
   extern __shared__ float sh_off[];          // [iters][2][B]
   __shared__ float2 red[2][WAVES * B];
   __shared__ float red_g[2][WAVES * B];
+  __shared__ __attribute__((aligned(16))) float ccb[B];
   const int b = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l >> 4, lc = l & 15;
   const int row0 = 16 * w + 4 * lr;          // this lane's rows row0 .. row0 + 3
@@ -238,7 +269,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
 #pragma unroll
       for (int c = 0; c < CPL; ++c) z[a][c] = z0[a][c];
     for (int it = 0; it < iters; ++it)
-      sk_iter<B>(z, red[it & 1], sh_off + (2 * it) * B, sh_off + (2 * it + 1) * B, w, lr, lc);
+      sk_iter<B>(z, red[it & 1], ccb, sh_off + (2 * it) * B, sh_off + (2 * it + 1) * B, w, lr, lc);
   }
   __syncthreads();
 
