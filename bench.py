@@ -57,6 +57,8 @@ def parse():
                     help="training step: the backward with the fused AdamW update of the logits")
     ap.add_argument("--saturate", action="store_true",
                     help="also time the Sinkhorn and the N:M mask at saturating sizes (to stderr)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured into a HIP graph (reported beside the eager value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (HBM counter calibration)")
@@ -446,6 +448,20 @@ def main():
         print("  %-24s %8.4f" % ("layer_init", sum(a.elapsed_time(b) for a, b in init_ev) / reps), file=sys.stderr)
         for n in names:
             print("  %-24s %8.4f" % (n, sum(he.ms(a, b) for a, b in evs[n]) / reps), file=sys.stderr)
+    graph = None
+    if args.graph and not args.adamw:
+        g = sess.capture_step(logits, dlogits, setup=True)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = ev(), ev()
+        g0.record(stream)
+        for _ in range(K):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / K
+        graph = {"ms_per_step": round(gms, 4), "value": round(1000.0 / gms, 2), "unit": "steps/s"}
     if args.saturate:
         sat = saturating_kernels(lcp, torch, he)
         print("saturating sizes: " + json.dumps(sat), file=sys.stderr)
@@ -482,6 +498,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if graph is not None:
+        out["graph"] = graph
     print(json.dumps(out), flush=True)
 
 

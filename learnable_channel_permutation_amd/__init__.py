@@ -76,6 +76,29 @@ class LayerSession:
         lcp_step_bwd(self.layer, logits, self.cfg, self.ws, dlogits, timing, stream)
         return dlogits
 
+    def capture_step(self, logits, dlogits, setup=True):
+        """Capture one step on fixed buffers into a HIP graph
+        (torch.cuda.CUDAGraph): the per-layer setup (when `setup`), the
+        forward (E into self.err) and the backward (into `dlogits`). The
+        library allocates nothing, synchronises nothing and issues no memset
+        inside a step, so the captured kernels are exactly the eager ones;
+        graph.replay() reruns them on the current contents of the buffers."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):           # one eager run before capture
+            if setup:
+                self.init()
+            self.forward(logits)
+            self.backward(logits, dlogits)
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            if setup:
+                self.init()
+            self.forward(logits)
+            self.backward(logits, dlogits)
+        return g
+
     def train(self, logits, steps, lr, tau0=1.0, tau1=0.1, beta1=0.9, beta2=0.999, eps=1e-8,
               weight_decay=0.01, stream=None):
         """`steps` AdamW steps on `logits` (updated in place) with the
