@@ -412,6 +412,32 @@ def test_step_hardened(ci, cout, cin, T):
     assert r < 2e-2, r
 
 
+def test_step_hardened_full_size_bench_layer():
+    """The hardened step (Method 2 forward, straight-through backward) on the
+    full 4096 x 11008 layer against the full float64 oracle: the hard P
+    exactly, the mask, E and the gradient."""
+    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    lay = lcp_synth.make_layer(spec)
+    lg, _ = lcp_synth.planted_logits(550, lay.cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
+    say("step hardened full size", spec.name)
+    s = lcp.LayerSession(up(lay.W, torch.bfloat16), up(lay.X, torch.bfloat16), spec.B, spec.iters, spec.tau,
+                         spec.N, spec.M, harden=True)
+    d_lg = up(lg)
+    P = torch.empty_like(d_lg)
+    bits = empty_bits(lay.cout, lay.cin)
+    err = s.forward(d_lg, P_out=P, bits_out=bits)
+    dl = s.backward(d_lg)
+    torch.cuda.synchronize()
+    fw = oracle.step_forward(lay.W, lay.X, lg, spec.tau, spec.iters, spec.N, spec.M, hard=True)
+    assert np.array_equal(down(P), fw["P"])
+    agree = bit_agreement(bits_down(bits), oracle.pack_bits(fw["mask"]), lay.cout * lay.cin)
+    assert agree >= 0.999, agree
+    assert abs(float(err.item()) - fw["E"]) / fw["E"] < 1e-2
+    bw = oracle.step_backward(fw, lay.X, lay.W)
+    r = rel_fro(down(dl), bw["dlogits"])
+    assert r < 2e-2, r
+
+
 # ------------------------------------------------------------ optimiser --
 def test_adamw_kernel():
     """lcp_adamw against the oracle's AdamW (float64) after three steps."""
