@@ -160,12 +160,13 @@ def _blas_threads():
 
 def cpu_baseline(spec, lay, hard=False, loss="frobenius", mask_ste=False):
     """The float64 oracle, untuned, for full forward + backward steps of the
-    same layer on the host cores: the median of 3 steps (1 for layers above
-    10^8 weights)."""
+    same layer on the host cores: the median step time of repeated steps,
+    repeated until about 10 s of work (at least 3 steps, a single step for
+    layers above 10^8 weights)."""
     import oracle
-    reps = 3 if spec.cout * spec.cin <= 10 ** 8 else 1
+    big = spec.cout * spec.cin > 10 ** 8
     times = []
-    for _ in range(reps):
+    while not times or (not big and (len(times) < 3 or sum(times) < 10.0) and len(times) < 200):
         t0 = time.perf_counter()
         fw = oracle.step_forward(lay.W, lay.X, lay.logits, spec.tau, spec.iters, spec.N, spec.M, hard=hard,
                                  loss=loss)
@@ -175,24 +176,26 @@ def cpu_baseline(spec, lay, hard=False, loss="frobenius", mask_ste=False):
     dt = float(np.median(times))
     return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(_blas_threads()), "cpu_count": os.cpu_count(),
             "kind": "oracle",
-            "sample": "median of %d full %s steps of the same %dx%d layer (T=%d), float64 NumPy, %.1f s each"
-                      % (reps, "forward+backward" if spec.backward else "forward", spec.cout, spec.cin, spec.T, dt)}
+            "sample": "median of %d full %s steps of the same %dx%d layer (T=%d), float64 NumPy, %.3f s each, %.1f s total"
+                      % (len(times), "forward+backward" if spec.backward else "forward", spec.cout, spec.cin, spec.T,
+                         dt, sum(times))}
 
 
 def cpu_baseline_deploy(W, X, P, mask):
     """The float64 oracle's deployed-layer forward on the host cores: the
-    median of 5 full forwards of the same layer."""
+    median of repeated full forwards of the same layer (about 10 s of work,
+    at least 3)."""
     import oracle
     times = []
-    for _ in range(5):
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 200):
         t0 = time.perf_counter()
         oracle.deploy_forward(W, X, P, mask)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     return {"value": 1.0 / dt, "unit": "forwards/s", "cores": int(_blas_threads()), "cpu_count": os.cpu_count(),
             "kind": "oracle",
-            "sample": "median of 5 full deployed-layer forwards (%dx%d weight, %d tokens), float64 NumPy, %.2f s each"
-                      % (W.shape[0], W.shape[1], X.shape[0], dt)}
+            "sample": "median of %d full deployed-layer forwards (%dx%d weight, %d tokens), float64 NumPy, %.3f s each, %.1f s total"
+                      % (len(times), W.shape[0], W.shape[1], X.shape[0], dt, sum(times))}
 
 
 def run_deploy(args, torch, lcp, lcp_synth):
