@@ -205,3 +205,42 @@ def test_deploy_argument_validation():
     assert lib.lcp_deploy_forward(p, p, p, 64, p, 8, 64, 128, p + 4096, p, s) == L.LCP_E_INVAL   # Y aliases X
     assert lib.lcp_deploy_forward(p, p, p, 64, p, 8, 64, 128, p, p + 4096, s) == L.LCP_E_INVAL   # Xp aliases X
     assert lib.lcp_deploy_forward(p, p, p, 32, p, 8, 60, 128, p + 4096, p + 8192, s) == L.LCP_E_INVAL
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/lcp.h compiles as C99 (gcc, warnings as errors), and a C
+    program that takes the address of every declared entry point links
+    against liblcp.so and runs its host-side checks (no GPU calls)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    L = _lib()
+    names = _declared()
+    src = ["#include <stdio.h>", "#include <string.h>", '#include "lcp.h"', "",
+           "int main(void) {",
+           "  void* fns[] = {" + ", ".join("(void*)&" + n for n in names) + "};",
+           "  size_t i, n = sizeof fns / sizeof fns[0];",
+           "  for (i = 0; i < n; ++i) if (!fns[i]) return 2;",
+           "  if (lcp_version() <= 0) return 3;",
+           "  if (strlen(lcp_status_string(LCP_E_INVAL)) == 0) return 4;",
+           "  size_t bytes = 0;",
+           "  if (lcp_step_workspace_bytes(4096, 11008, 2048, 64, 5, LCP_BF16, &bytes) != LCP_OK || bytes == 0) return 5;",
+           "  if (lcp_sinkhorn(0, 0, 1, 64, 5, 1.0f, 0) != LCP_E_INVAL) return 6;",
+           "  lcp_cfg c; memset(&c, 0, sizeof c); c.iters = 5; c.tau = 1.0f; c.N = 2; c.M = 4;",
+           "  c.loss = LCP_LOSS_COSINE;",
+           "  if (lcp_step_fwd(0, 0, &c, 0, 0, 0, 0, 0, 0, 0) != LCP_E_INVAL) return 7;",
+           '  printf("ok %u\\n", (unsigned)n);',
+           "  return 0;", "}"]
+    cfile = tmp_path / "abi_check.c"
+    cfile.write_text("\n".join(src) + "\n")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(L._LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(cfile),
+           "-L", libdir, "-llcp", "-Wl,-rpath," + libdir, "-o", str(exe)]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    assert p.returncode == 0, p.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.strip() == "ok %d" % len(names)
