@@ -77,12 +77,21 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """Source text without comments and blank lines (a comment edit does not
+    change the kernel the counters were taken on)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "learnable_channel_permutation_amd", "csrc")
     for f in ["common.h"] + sorted(KERNEL_SOURCES.get(kernel, [])):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,7 +1,8 @@
 // GEMMs of the LCP step: the output error R = D X^T (E = ||R||_F) and the
-// backward product dD = (1/E) R X, both written as C[m][n] = sum_k A[m][k] B[n][k]
-// with A and B row-major and K contiguous (the backward reads X transposed,
-// prepared once per layer).
+// backward product G = dL/dW_tilde = c A X (A = R with c = -1/E for the
+// Frobenius objective, A = dL/dY~ with c = 1 for the cosine objective), both
+// written as C[m][n] = sum_k A[m][k] B[n][k] with A and B row-major and K
+// contiguous (the backward reads X transposed, prepared once per layer).
 //
 // bf16 kernel (gfx950): BM x BN x 64 tiles, 8 waves (two per SIMD) in a
 // 4 x 2 layout, each wave owning (BM/4) x (BN/2) of the tile as MFMA 32x32x16
