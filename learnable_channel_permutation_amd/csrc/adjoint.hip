@@ -1,15 +1,16 @@
-// Block adjoint of the LCP forward with the mask held constant.
+// Block adjoint of the LCP forward (mask held constant unless the
+// straight-through term below is on).
 //
 // Forward (per block b): W_hat_b = W_b P_b, A_b = W_hat_b . M_b,
-// W_tilde_b = A_b P_b^T. Given G = dE/dW_tilde (= -dE/dD), the chain rule gives
-//   dE/dP_b = G_b^T A_b + W_b^T ((G_b P_b) . M_b),
+// W_tilde_b = A_b P_b^T. Given G = dL/dW_tilde (= -dL/dD), the chain rule gives
+//   dL/dP_b = G_b^T A_b + W_b^T ((G_b P_b) . M_b),
 // a sum over the Cout rows. Each workgroup reduces one block over one chunk of
 // rows and writes that partial B x B matrix; the Sinkhorn adjoint kernel adds
 // the chunk partials in chunk order (deterministic, no atomics).
 //
-// bf16 kernel: each wave runs its own pipeline over 32-row tiles of W and G.
-// Tiles move HBM -> LDS with 16-byte direct-to-LDS loads into a private
-// two-stage ring (no register staging, no workgroup barriers in the loop);
+// bf16 kernel (B <= 64): each wave runs its own pipeline over 32-row tiles of
+// W and G. Tiles move HBM -> LDS with 16-byte direct-to-LDS loads into a
+// private two-stage ring (no register staging, no workgroup barriers in the loop);
 // load instruction (matrix, K step p) of a tile has lane l fetch exactly the
 // 16 bytes that lane l later feeds to the MFMA for that K step, so the LDS
 // reads are linear and conflict-free. Rows are remapped so that MFMA outputs
