@@ -252,6 +252,28 @@ def test_step_small(ci, cout, cin, T):
     _check_step(lay, spec, got)
 
 
+TINY = [
+    # (config index, cout, cin, T): one output row, one token, one block,
+    # sizes one past a tile boundary
+    (2, 1, 64, 1),
+    (2, 3, 128, 7),
+    (2, 33, 64, 65),
+    (0, 1, 32, 1),
+    (0, 5, 64, 3),
+    (3, 2, 128, 2),
+]
+
+
+@pytest.mark.parametrize("ci,cout,cin,T", TINY)
+def test_step_tiny_shapes(ci, cout, cin, T):
+    """Degenerate sizes: the guards and clamps of every kernel of the step."""
+    spec = lcp_synth.CONFIGS[ci]
+    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
+    say("step tiny", spec.name, cout, cin, T)
+    got = _run_step(lay, spec)
+    _check_step(lay, spec, got, e_tol=1e-2 if spec.dtype == "bf16" else 1e-4)
+
+
 def test_step_c1_fp32_full_size():
     """The 256 x 256 float32 layer at its full size, forward and backward."""
     spec = lcp_synth.CONFIGS[0]
