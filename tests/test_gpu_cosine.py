@@ -149,6 +149,16 @@ def test_step_cosine_full_size_bench_layer():
     _check(lay, spec, lay.logits, "cosine", True, False)
 
 
+def test_step_cosine_ste_hardened_full_size_b128():
+    """The 13824 x 5120 layer (B = 128, 4:8) at full size with every option:
+    hardened forward, cosine objective, the mask's straight-through term."""
+    spec = lcp_synth.CONFIGS[3]
+    lay = lcp_synth.make_layer(spec)
+    lg, _ = lcp_synth.planted_logits(650, lay.cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
+    say("step cosine ste hardened full size", spec.name)
+    _check(lay, spec, lg, "cosine", True, True)
+
+
 def test_training_cosine_beats_wanda():
     """lcp_train on the cosine objective (hardened forward, straight-through
     backward through P, mask constant): the first step is plain Wanda's
