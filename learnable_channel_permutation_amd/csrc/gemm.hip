@@ -28,6 +28,8 @@
 // writes one sum of Y . C per workgroup, Y a matrix of C's layout (the dense
 // layer outputs of the cosine objective); DD scales by a factor read from
 // device memory (written by the finalisation kernel) and stores bf16.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -239,6 +241,227 @@ __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
   }
 }
 
+// ---- error GEMM: software-pipelined ring ---------------------------------------
+// 256 x 128 tiles, 8 waves (4 x 2, each 64 x 64), three-stage direct-to-LDS
+// ring of 64-wide K steps. Two things keep the MFMA arrays fed:
+//  * the loads of tile kt + 2 are not issued in one burst after the barrier
+//    (which stalls every wave on the vector-memory queue at the same time)
+//    but one at a time between the MFMAs of step kt;
+//  * the step's barrier sits before its last 16-wide sub-step: the wave
+//    waits for its own loads of tile kt + 1, meets the others, issues the
+//    first fragment reads of tile kt + 1 and only then runs the last
+//    sub-step's MFMAs, whose operands are already in registers. The barrier
+//    and the LDS latency hide under those MFMAs.
+// The barrier of step kt also retires stage kt - 1 (every wave has read its
+// last fragments of it), which step kt + 1 refills with tile kt + 3.
+// MF selects the MFMA: 32 (32x32x16, lane holds 16 consecutive columns of a
+// row) or 16 (16x16x32, lane holds 4 consecutive columns of a row).
+constexpr int RS = 3;   // ring stages
+
+template <int EPI, int MF>
+__global__ __launch_bounds__(GNT, 1) void gemm_err_kernel(
+    const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M,
+    int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, float* __restrict__ part,
+    const uint16_t* __restrict__ Yc, float* __restrict__ part2) {
+  constexpr int BM = 256, BN = 128;
+  constexpr int WM = BM / GWM, WN = BN / GWN;
+  constexpr int FM = WM / MF, FN = WN / MF, NM = FM * FN;
+  constexpr int KS = MF == 32 ? 16 : 32;                   // K per MFMA
+  constexpr int P = GBK / KS;                              // sub-steps per K step
+  constexpr int AI = BM * 8 / GNT, BI = BN * 8 / GNT, NL = AI + BI;
+  constexpr int STAGE = (BM + BN) * GBK;
+  static_assert(P % 2 == 0, "fragment double buffer alternates within a step");
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N_store + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  const int wm = w / GWN, wn = w % GWN;
+  // fragment lane roles: MF 32: K half h, row ln; MF 16: K quarter q, row l16
+  const int kq = MF == 32 ? (l >> 5) : (l >> 4);
+  const int lr = MF == 32 ? (l & 31) : (l & 15);
+
+  // load q of this thread for the tile at k0 into stage `stage`
+  auto issue_one = [&](int stage, int k0, int q) {
+    uint16_t* sb = lds + stage * STAGE;
+    if (q < AI) {
+      const int c = (q * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+      const int gm = min(m0 + row, M - 1), gk = k0 + ch * 8;
+      const void* src = (gk < K) ? (const void*)(A + (size_t)gm * lda + gk) : (const void*)g_zero16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + (q * GNW + w) * 64 * 8), 16, 0, 0);
+    } else {
+      const int qb = q - AI;
+      const int c = (qb * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+      const int gn = n0 + row, gk = k0 + ch * 8;
+      const void* src = (gk < K && gn < N_valid) ? (const void*)(Bm + (size_t)gn * ldb + gk) : (const void*)g_zero16;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + BM * GBK + (qb * GNW + w) * 64 * 8), 16, 0, 0);
+    }
+  };
+
+  typedef typename std::conditional<MF == 32, floatx16, floatx4>::type acc_t;
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{};
+  int arow[FM], brow[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) arow[i] = wm * WM + i * MF + lr;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) brow[j] = wn * WN + j * MF + (MF == 32 ? remap_row(lr) : lr);
+
+  u32x4 fa[2][FM], fb[2][FN];
+  auto rd = [&](int stage, int p, int fs) {
+    const uint16_t* As = lds + stage * STAGE;
+    const uint16_t* Bs = As + BM * GBK;
+    const int ch = (KS / 8) * p + kq;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[fs][i] = *reinterpret_cast<const u32x4*>(&As[swz(arow[i], ch)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[fs][j] = *reinterpret_cast<const u32x4*>(&Bs[swz(brow[j], ch)]);
+  };
+  auto mma = [&](int fs, int m) {
+    const int i = m / FN, j = m % FN;
+    if constexpr (MF == 32) acc[i][j] = mfma32(fb[fs][j], fa[fs][i], acc[i][j]);
+    else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fb[fs][j]), as_bf16x8(fa[fs][i]), acc[i][j], 0, 0, 0);
+  };
+  // step on stage `stage`: with LOAD the tile at k0 goes to stage `lstage`
+  // between the MFMAs of sub-steps 0 .. P-2; with NEXT the first fragments of
+  // stage `nstage` are read after the barrier. WAIT1: one tile's loads (the
+  // ones just issued) may stay in flight at the barrier.
+  auto step = [&](int stage, int lstage, int k0, int nstage, auto LOAD, auto NEXT, auto WAIT1) {
+    constexpr bool DL = decltype(LOAD)::value, DN = decltype(NEXT)::value;
+    constexpr int SLOTS = (P - 1) * NM;
+#pragma unroll
+    for (int p = 0; p < P - 1; ++p) {
+      __builtin_amdgcn_sched_barrier(0);
+      rd(stage, p + 1, (p + 1) & 1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+#pragma unroll
+        for (int o = 0; o < (DL ? NL : 0); ++o)
+          if (o * SLOTS / NL == p * NM + m) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(lstage, k0, o);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        mma(p & 1, m);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(WAIT1)::value) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DN) rd(nstage, 0, 0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) mma((P - 1) & 1, m);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  typedef std::true_type Y_;
+  typedef std::false_type N_;
+
+  const int nk = (K + GBK - 1) / GBK;
+  // tiles 0 and 1 (a tile past K reads zeros and is never multiplied)
+#pragma unroll
+  for (int q = 0; q < NL; ++q) issue_one(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < NL; ++q) issue_one(1, GBK, q);
+  wait_vmcnt<NL>();
+  __builtin_amdgcn_s_barrier();
+  rd(0, 0, 0);
+  int kt = 0;
+  for (; kt + 5 < nk; kt += 3) {
+    step(0, 2, (kt + 2) * GBK, 1, Y_{}, Y_{}, Y_{});
+    step(1, 0, (kt + 3) * GBK, 2, Y_{}, Y_{}, Y_{});
+    step(2, 1, (kt + 4) * GBK, 0, Y_{}, Y_{}, Y_{});
+  }
+  for (; kt < nk; ++kt) {                                  // the last 1 .. 5 tiles
+    const int st = kt % RS;
+    if (kt + 2 < nk) {
+      if (st == 0) step(0, 2, (kt + 2) * GBK, 1, Y_{}, Y_{}, Y_{});
+      else if (st == 1) step(1, 0, (kt + 2) * GBK, 2, Y_{}, Y_{}, Y_{});
+      else step(2, 1, (kt + 2) * GBK, 0, Y_{}, Y_{}, Y_{});
+    } else if (kt + 1 < nk) {
+      if (st == 0) step(0, 0, 0, 1, N_{}, Y_{}, N_{});
+      else if (st == 1) step(1, 0, 0, 2, N_{}, Y_{}, N_{});
+      else step(2, 0, 0, 0, N_{}, Y_{}, N_{});
+    } else {
+      if (st == 0) step(0, 0, 0, 0, N_{}, N_{}, N_{});
+      else if (st == 1) step(1, 0, 0, 0, N_{}, N_{}, N_{});
+      else step(2, 0, 0, 0, N_{}, N_{}, N_{});
+    }
+  }
+  wait_vmcnt<0>();                                         // the zero tile of a one-tile K
+
+  // ---- epilogue. MF 32: lane (h, ln) of block (i, j) holds row
+  // m0 + wm*WM + 32i + ln, columns n0 + wn*WN + 32j + 16h + r (r < 16).
+  // MF 16: lane (q, l16) holds row m0 + wm*WM + 16i + l16, columns
+  // n0 + wn*WN + 16j + 4q + r (r < 4).
+  constexpr int CPL = MF == 32 ? 16 : 4;                   // consecutive columns per lane
+  float ss = 0.f, sy = 0.f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WM + MF * i + lr;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nb = n0 + wn * WN + MF * j + CPL * kq;
+      const acc_t a = acc[i][j];
+      if (m < M) {   // rows past M were read from a clamped row
+#pragma unroll
+        for (int r = 0; r < CPL; ++r) ss += a[r] * a[r];
+      }
+      if (m < M && nb < N_store) {
+        if constexpr (MF == 32) {
+          if (EPI == EPI_ERRCOS) {
+            const u32x4* ys = reinterpret_cast<const u32x4*>(Yc + (size_t)m * ldc + nb);
+            const u32x4 y0 = ys[0], y1 = ys[1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              sy += lo_bf(y0[q]) * a[2 * q] + hi_bf(y0[q]) * a[2 * q + 1];
+              sy += lo_bf(y1[q]) * a[8 + 2 * q] + hi_bf(y1[q]) * a[8 + 2 * q + 1];
+            }
+          }
+          u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)m * ldc + nb);
+          dst[0] = u32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7])};
+          dst[1] = u32x4{pack2(a[8], a[9]), pack2(a[10], a[11]), pack2(a[12], a[13]), pack2(a[14], a[15])};
+        } else {
+          if (EPI == EPI_ERRCOS) {
+            const uint2 y = *reinterpret_cast<const uint2*>(Yc + (size_t)m * ldc + nb);
+            sy += lo_bf(y.x) * a[0] + hi_bf(y.x) * a[1] + lo_bf(y.y) * a[2] + hi_bf(y.y) * a[3];
+          }
+          *reinterpret_cast<uint2*>(C + (size_t)m * ldc + nb) = uint2{pack2(a[0], a[1]), pack2(a[2], a[3])};
+        }
+      }
+    }
+  }
+  __syncthreads();                                         // the ring is no longer read
+  float* wsum = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) ss += shfl_xor(ss, x);
+  if (EPI == EPI_ERRCOS) {
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) sy += shfl_xor(sy, x);
+  }
+  if (l == 0) {
+    wsum[w] = ss;
+    wsum[GNW + w] = sy;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float tot = 0.f, toty = 0.f;
+    for (int i = 0; i < GNW; ++i) {
+      tot += wsum[i];
+      toty += wsum[GNW + i];
+    }
+    part[blockIdx.x] = tot;
+    if (EPI == EPI_ERRCOS) part2[blockIdx.x] = toty;
+  }
+}
+
 // ---- fp32 VALU GEMM ------------------------------------------------------------
 // 64 x 64 tiles, 16 x 16 threads, 4 x 4 outputs per thread, K step 16.
 // B_NN = 0: B is [N][K] (ldb); B_NN = 1: B is [K][N] (ldb).
@@ -338,9 +561,10 @@ __global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restr
 
 // ---- launchers -------------------------------------------------------------------
 // error GEMM: 256 x 128 tiles (the 4096 x 2048 residual is exactly 256 tiles)
-// with a three-stage ring (144 KB of LDS; its long K loop streams more
-// operand bytes per flop); dD GEMM: 256 x 256 tiles, two stages (128 KB).
-constexpr int EBM = 256, EBN = 128, ES = 3, DBM = 256, DBN = 256, DS = 2;
+// in the pipelined three-stage ring (144 KB of LDS); dD GEMM: 256 x 256
+// tiles, two stages (128 KB).
+constexpr int EBM = 256, EBN = 128, DBM = 256, DBN = 256, DS = 2;
+constexpr int EMF = 32;   // MFMA of the error GEMM
 
 int gemm_error_parts(int M, int N, int bf16) {
   if (bf16) return ((M + EBM - 1) / EBM) * ((N + EBN - 1) / EBN);
@@ -351,12 +575,13 @@ hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm
                                   int N_valid, int N_store, int K, uint16_t* C, int ldc,
                                   float* part, const uint16_t* Y, float* party, hipStream_t s) {
   const int G = gemm_error_parts(M, N_store, 1);
+  constexpr size_t lds = gemm_lds_bytes<EBM, EBN, RS>();
   if (Y)
-    gemm_bf16_kernel<EBM, EBN, EPI_ERRCOS, ES><<<G, GNT, gemm_lds_bytes<EBM, EBN, ES>(), s>>>(
-        A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr, Y, party);
+    gemm_err_kernel<EPI_ERRCOS, EMF><<<G, GNT, lds, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc,
+                                                         part, Y, party);
   else
-    gemm_bf16_kernel<EBM, EBN, EPI_ERR, ES><<<G, GNT, gemm_lds_bytes<EBM, EBN, ES>(), s>>>(
-        A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr, nullptr, nullptr);
+    gemm_err_kernel<EPI_ERR, EMF><<<G, GNT, lds, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc,
+                                                      part, nullptr, nullptr);
   return hipGetLastError();
 }
 
