@@ -564,7 +564,7 @@ __global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restr
 // in the pipelined three-stage ring (144 KB of LDS); dD GEMM: 256 x 256
 // tiles, two stages (128 KB).
 constexpr int EBM = 256, EBN = 128, DBM = 256, DBN = 256, DS = 2;
-constexpr int EMF = 32;   // MFMA of the error GEMM
+constexpr int EMF = 16;   // MFMA of the error GEMM
 
 int gemm_error_parts(int M, int N, int bf16) {
   if (bf16) return ((M + EBM - 1) / EBM) * ((N + EBN - 1) / EBN);
