@@ -4,24 +4,25 @@
 // written as C[m][n] = sum_k A[m][k] B[n][k] with A and B row-major and K
 // contiguous (the backward reads X transposed, prepared once per layer).
 //
-// bf16 kernel (gfx950): BM x BN x 64 tiles, 8 waves (two per SIMD) in a
-// 4 x 2 layout, each wave owning (BM/4) x (BN/2) of the tile as MFMA 32x32x16
-// blocks with fp32 accumulators. Operand tiles move global -> LDS with
-// 16-byte direct-to-LDS loads (no register staging) into a two- or
-// three-stage ring; one barrier per K step, and the next tiles' loads are in
-// flight while the current one is multiplied. Chunk c of row r is stored at position
-// c ^ ((r >> 1) & 7): the 16-byte fragment reads of 16 consecutive rows then
-// cover all 64 LDS banks. Inside a K step the MFMAs of one 16-wide sub-step
-// are interleaved one-to-one with the fragment reads of the next
-// (sched_group_barrier), so LDS latency hides under MFMA work. The MFMA A
-// operand is taken from the B matrix with the row remap of common.h, so each
-// lane ends up holding 16 consecutive output columns of one output row and
-// writes them as two 16-byte stores. Workgroups are ordered so that each XCD
-// (workgroup id mod 8) works on a compact group of 4 row panels x N column
-// panels, which keeps the panels shared inside that XCD's L2.
+// bf16 kernels (gfx950): BM x BN x 64 tiles, 8 waves (two per SIMD) in a
+// 4 x 2 layout, each wave owning (BM/4) x (BN/2) of the tile as MFMA blocks
+// with fp32 accumulators. Operand tiles move global -> LDS with 16-byte
+// direct-to-LDS loads (no register staging) into a ring of stages. Chunk c
+// of row r is stored at position c ^ ((r >> 1) & 7): the 16-byte fragment
+// reads of 16 consecutive rows then cover all 64 LDS banks. The MFMA A
+// operand is taken from the B matrix, so each lane ends up holding
+// consecutive output columns of one output row. Workgroups are ordered so
+// that each XCD (workgroup id mod 8) works on a compact group of 4 row panels
+// x N column panels, which keeps the panels shared inside that XCD's L2.
 // Out-of-range rows are read from a clamped row (their outputs are never
 // stored); out-of-range K chunks and B rows read a 16-byte zero block, so
 // padded output columns come out exactly zero.
+//  * gemm_bf16_kernel (the backward product): a two-stage ring on 32x32x16
+//    MFMAs, one barrier per K step after which the next tile's loads are
+//    issued; inside a step the MFMAs of one 16-wide sub-step are interleaved
+//    one-to-one with the fragment reads of the next (sched_group_barrier).
+//  * gemm_err_kernel (the error product): a software-pipelined three-stage
+//    ring on 16x16x32 MFMAs, described at the kernel.
 //
 // Epilogues: ERR stores C in bf16 and one sum of squares of the fp32
 // accumulators per workgroup (reduced later in a fixed order); ERRCOS also
