@@ -204,6 +204,29 @@ def test_error_gemm(dtype, cout, cin, T):
     assert np.all(Rg[:, T:] == 0)
 
 
+@pytest.mark.parametrize("cin", list(range(32, 545, 32)))
+def test_error_gemm_k_tails(cin):
+    """bf16 error GEMM over every count of 64-wide K steps from 1 to 9 (the
+    software-pipelined ring has separate paths for the last 1 .. 5 steps),
+    whole and half last steps, with ragged rows (257) and tokens (130)."""
+    cout, T = 257, 130
+    W = lcp_synth.random_matrix(40 + cin, (cout, cin), std=0.02, dtype="bf16")
+    Wt = lcp_synth.random_matrix(41 + cin, (cout, cin), std=0.02, dtype="bf16")
+    X = lcp_synth.random_matrix(42 + cin, (T, cin), std=1.0, dtype="bf16")
+    say("error gemm k tails", cin)
+    ws = torch.empty(L.lcp_error_workspace_bytes(cout, cin, T, L.LCP_BF16), dtype=torch.uint8, device=DEV)
+    err = torch.empty(1, dtype=torch.float32, device=DEV)
+    pitch = L.lcp_xt_pitch(T)
+    R = torch.full((cout, pitch), 3.0, dtype=torch.bfloat16, device=DEV)
+    L.lcp_error(up(W, torch.bfloat16), up(Wt, torch.bfloat16), up(X, torch.bfloat16), err, ws, R_out=R)
+    torch.cuda.synchronize()
+    Rref, Eref = oracle.pruning_error(W.astype(np.float64) - Wt, X)
+    Rg = down(R)
+    assert abs(float(err.item()) - Eref) / Eref < 1e-2
+    assert rel_fro(Rg[:, :T], Rref) < 1e-2
+    assert np.all(Rg[:, T:] == 0)
+
+
 # --------------------------------------------------------------- full step --
 def _run_step(lay, spec, backward=True, dtype=None):
     dtype = dtype or spec.dtype
