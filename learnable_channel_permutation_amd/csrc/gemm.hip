@@ -17,7 +17,7 @@
 // Out-of-range rows are read from a clamped row (their outputs are never
 // stored); out-of-range K chunks and B rows read a 16-byte zero block, so
 // padded output columns come out exactly zero.
-//  * gemm_bf16_kernel (the backward product): a two-stage ring on 32x32x16
+//  * gemm_dd_kernel (the backward product): a two-stage ring on 32x32x16
 //    MFMAs, one barrier per K step after which the next tile's loads are
 //    issued; inside a step the MFMAs of one 16-wide sub-step are interleaved
 //    one-to-one with the fragment reads of the next (sched_group_barrier).
@@ -89,11 +89,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int EPI, int S>
-__global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
+// The backward product C = coef[1] * A B^T (bf16 out).
+template <int BM, int BN, int S>
+__global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M,
-    int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, float* __restrict__ part,
-    const float* __restrict__ Eptr, const uint16_t* __restrict__ Yc, float* __restrict__ part2) {
+    int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, const float* __restrict__ Eptr) {
   constexpr int WM = BM / GWM, WN = BN / GWN, FM = WM / 32, FN = WN / 32;
   constexpr int AI = BM * 8 / GNT, BI = BN * 8 / GNT;     // 16-byte loads per thread per tile
   constexpr int STAGE = (BM + BN) * GBK;                   // bf16 elements per ring stage
@@ -184,9 +184,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
 
   // ---- epilogue: lane (h, ln) of block (i, j) holds row m0 + wm*WM + 32i + ln,
   // columns n0 + wn*WN + 32j + 16h + r, r < 16.
-  constexpr bool ERRS = EPI == EPI_ERR || EPI == EPI_ERRCOS;
-  const float scale = (EPI == EPI_DD) ? Eptr[1] : 1.f;
-  float ss = 0.f, sy = 0.f;
+  const float scale = Eptr[1];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * WM + 32 * i + ln;
@@ -194,50 +192,13 @@ __global__ __launch_bounds__(GNT, 1) void gemm_bf16_kernel(
     for (int j = 0; j < FN; ++j) {
       const int nb = n0 + wn * WN + 32 * j + 16 * h;
       const floatx16 a = acc[i][j];
-      if (ERRS && m < M) {   // rows past M were read from a clamped row
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ss += a[r] * a[r];
-      }
-      if (EPI == EPI_ERRCOS && m < M && nb < N_store) {
-        const u32x4* ys = reinterpret_cast<const u32x4*>(Yc + (size_t)m * ldc + nb);
-        const u32x4 y0 = ys[0], y1 = ys[1];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          sy += lo_bf(y0[q]) * a[2 * q] + hi_bf(y0[q]) * a[2 * q + 1];
-          sy += lo_bf(y1[q]) * a[8 + 2 * q] + hi_bf(y1[q]) * a[8 + 2 * q + 1];
-        }
-      }
-      if (m < M && nb < N_store) {
+      if (m < M && nb < N_store) {   // rows past M were read from a clamped row
         u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)m * ldc + nb);
         dst[0] = u32x4{pack2(a[0] * scale, a[1] * scale), pack2(a[2] * scale, a[3] * scale),
                        pack2(a[4] * scale, a[5] * scale), pack2(a[6] * scale, a[7] * scale)};
         dst[1] = u32x4{pack2(a[8] * scale, a[9] * scale), pack2(a[10] * scale, a[11] * scale),
                        pack2(a[12] * scale, a[13] * scale), pack2(a[14] * scale, a[15] * scale)};
       }
-    }
-  }
-  if (ERRS) {
-    __syncthreads();                                   // the ring is no longer read
-    float* wsum = reinterpret_cast<float*>(lds);
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) ss += shfl_xor(ss, x);
-    if (EPI == EPI_ERRCOS) {
-#pragma unroll
-      for (int x = 32; x >= 1; x >>= 1) sy += shfl_xor(sy, x);
-    }
-    if (l == 0) {
-      wsum[w] = ss;
-      wsum[GNW + w] = sy;
-    }
-    __syncthreads();
-    if (t == 0) {
-      float tot = 0.f, toty = 0.f;
-      for (int i = 0; i < GNW; ++i) {
-        tot += wsum[i];
-        toty += wsum[GNW + i];
-      }
-      part[blockIdx.x] = tot;
-      if (EPI == EPI_ERRCOS) part2[blockIdx.x] = toty;
     }
   }
 }
@@ -589,8 +550,8 @@ hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm
 hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
                                int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s) {
   const int G = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
-  gemm_bf16_kernel<DBM, DBN, EPI_DD, DS><<<G, GNT, gemm_lds_bytes<DBM, DBN, DS>(), s>>>(
-      A, lda, Bm, ldb, M, N, N, K, C, ldc, nullptr, E, nullptr, nullptr);
+  gemm_dd_kernel<DBM, DBN, DS><<<G, GNT, gemm_lds_bytes<DBM, DBN, DS>(), s>>>(A, lda, Bm, ldb, M, N, N, K, C,
+                                                                           ldc, E);
   return hipGetLastError();
 }
 
