@@ -425,9 +425,13 @@ __global__ __launch_bounds__(GNT, 1) void gemm_err_kernel(
 }
 
 // ---- fp32 VALU GEMM ------------------------------------------------------------
-// 64 x 64 tiles, 16 x 16 threads, 4 x 4 outputs per thread, K step 16.
-// B_NN = 0: B is [N][K] (ldb); B_NN = 1: B is [K][N] (ldb).
-template <int EPI, int B_NN>
+// TS x TS tiles (TS = 64, or 32 for grids that would leave most CUs idle),
+// 16 x 16 threads, RPT x RPT outputs per thread, K step 16. Each thread loads
+// one VEC-float piece of the A tile and of the B tile per K step; the next
+// step's pieces are loaded into registers before the current step's FMAs,
+// so the global latency hides under them. B_NN = 0: B is [N][K] (ldb);
+// B_NN = 1: B is [K][N] (ldb).
+template <int EPI, int B_NN, int TS>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int lda,
                                                        const float* __restrict__ Bm, int ldb, int M,
                                                        int N_valid, int N_store, int K,
@@ -436,39 +440,98 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        const float* __restrict__ Eptr,
                                                        const float* __restrict__ Yc,
                                                        float* __restrict__ part2) {
-  __shared__ float as[16][64 + 1];
-  __shared__ float bs[16][64 + 1];
-  const int tiles_n = (N_store + 63) / 64;
-  const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
+  constexpr int KS = 16, RPT = TS / 16, VEC = TS * KS / 256;
+  constexpr int PAD = TS + 4;                               // keeps 16-byte alignment of LDS rows
+  __shared__ __attribute__((aligned(16))) float as[KS][PAD];
+  __shared__ __attribute__((aligned(16))) float bs[KS][PAD];
+  const int tiles_n = (N_store + TS - 1) / TS;
+  const int m0 = (blockIdx.x / tiles_n) * TS, n0 = (blockIdx.x % tiles_n) * TS;
   const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int e = t; e < 16 * 64; e += 256) {
-      const int kk = e & 15, r = e >> 4;
-      const int gm = m0 + r, gk = k0 + kk;
-      as[kk][r] = (gm < M && gk < K) ? A[(size_t)gm * lda + gk] : 0.f;
-      const int gn = n0 + r;
-      float bv = 0.f;
-      if (gn < N_valid && gk < K) bv = B_NN ? Bm[(size_t)gk * ldb + gn] : Bm[(size_t)gn * ldb + gk];
-      bs[kk][r] = bv;
+
+  // this thread's pieces: K-contiguous (row lr, K offset lk) or, for a [K][N]
+  // B, N-contiguous (K row bk, N offset bn)
+  constexpr int KPR = KS / VEC;                             // pieces per K-contiguous row
+  const int lr = t / KPR, lk = (t % KPR) * VEC;
+  constexpr int NPR = TS / VEC;                             // pieces per N-contiguous row
+  const int bk = t / NPR, bn = (t % NPR) * VEC;
+  float ra[VEC], rb[VEC];
+  auto load_k = [&](const float* base, int ld, int r, int rmax, int k0, float (&v)[VEC]) {
+    const int gk = k0 + lk;
+    if (r < rmax && gk + VEC <= K) {
+      const float* src = base + (size_t)r * ld + gk;
+      if constexpr (VEC == 4) {
+        const floatx4 q = *reinterpret_cast<const floatx4*>(src);
+        v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+      } else {
+        const float2 q = *reinterpret_cast<const float2*>(src);
+        v[0] = q.x; v[1] = q.y;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = (r < rmax && gk + e < K) ? base[(size_t)r * ld + gk + e] : 0.f;
     }
+  };
+  auto load = [&](int k0) {
+    load_k(A, lda, m0 + lr, M, k0, ra);
+    if constexpr (B_NN) {
+      const int gk = k0 + bk, gn = n0 + bn;
+      if (gk < K && gn + VEC <= N_valid) {
+        const float* src = Bm + (size_t)gk * ldb + gn;
+        if constexpr (VEC == 4) {
+          const floatx4 q = *reinterpret_cast<const floatx4*>(src);
+          rb[0] = q[0]; rb[1] = q[1]; rb[2] = q[2]; rb[3] = q[3];
+        } else {
+          const float2 q = *reinterpret_cast<const float2*>(src);
+          rb[0] = q.x; rb[1] = q.y;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) rb[e] = (gk < K && gn + e < N_valid) ? Bm[(size_t)gk * ldb + gn + e] : 0.f;
+      }
+    } else {
+      load_k(Bm, ldb, n0 + lr, N_valid, k0, rb);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) as[lk + e][lr] = ra[e];
+    if constexpr (B_NN) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) bs[bk][bn + e] = rb[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) bs[lk + e][lr] = rb[e];
+    }
+  };
+
+  float acc[RPT][RPT] = {};
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += KS) {
+    store();
     __syncthreads();
+    if (k0 + KS < K) load(k0 + KS);
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
+    for (int kk = 0; kk < KS; ++kk) {
+      float av[RPT], bv[RPT];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < RPT; ++a) av[a] = as[kk][ty * RPT + a];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(as[kk][ty * 4 + a], bs[kk][tx * 4 + c], acc[a][c]);
+      for (int c = 0; c < RPT; ++c) bv[c] = bs[kk][tx * RPT + c];
+#pragma unroll
+      for (int a = 0; a < RPT; ++a)
+#pragma unroll
+        for (int c = 0; c < RPT; ++c) acc[a][c] = fmaf(av[a], bv[c], acc[a][c]);
+    }
     __syncthreads();
   }
   constexpr bool ERRS = EPI == EPI_ERR || EPI == EPI_ERRCOS;
   const float scale = (EPI == EPI_DD) ? Eptr[1] : 1.f;
   float ss = 0.f, sy = 0.f;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < RPT; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int m = m0 + ty * 4 + a, n = n0 + tx * 4 + c;
+    for (int c = 0; c < RPT; ++c) {
+      const int m = m0 + ty * RPT + a, n = n0 + tx * RPT + c;
       if (ERRS) ss += acc[a][c] * acc[a][c];
       if (m < M && n < N_store) {
         C[(size_t)m * ldc + n] = acc[a][c] * scale;
@@ -528,9 +591,14 @@ __global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restr
 constexpr int EBM = 256, EBN = 128, DBM = 256, DBN = 256, DS = 2;
 constexpr int EMF = 16;   // MFMA of the error GEMM
 
+// fp32 tile size: 64, or 32 when 64-wide tiles would occupy fewer than 128
+// of the 256 CUs
+static int f32_tile(int M, int N) { return ((M + 63) / 64) * ((N + 63) / 64) < 128 ? 32 : 64; }
+
 int gemm_error_parts(int M, int N, int bf16) {
   if (bf16) return ((M + EBM - 1) / EBM) * ((N + EBN - 1) / EBN);
-  return ((M + 63) / 64) * ((N + 63) / 64);
+  const int ts = f32_tile(M, N);
+  return ((M + ts - 1) / ts) * ((N + ts - 1) / ts);
 }
 
 hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
@@ -559,19 +627,21 @@ hipError_t launch_gemm_error_f32(const float* A, int lda, const float* Bm, int l
                                  int N_valid, int N_store, int K, float* C, int ldc, float* part,
                                  const float* Y, float* party, hipStream_t s) {
   const int G = gemm_error_parts(M, N_store, 0);
+  const bool t32 = f32_tile(M, N_store) == 32;
   if (Y)
-    gemm_f32_kernel<EPI_ERRCOS, 0><<<G, 256, 0, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part,
-                                                      nullptr, Y, party);
+    (t32 ? gemm_f32_kernel<EPI_ERRCOS, 0, 32> : gemm_f32_kernel<EPI_ERRCOS, 0, 64>)<<<G, 256, 0, s>>>(
+        A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr, Y, party);
   else
-    gemm_f32_kernel<EPI_ERR, 0><<<G, 256, 0, s>>>(A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part,
-                                                   nullptr, nullptr, nullptr);
+    (t32 ? gemm_f32_kernel<EPI_ERR, 0, 32> : gemm_f32_kernel<EPI_ERR, 0, 64>)<<<G, 256, 0, s>>>(
+        A, lda, Bm, ldb, M, N_valid, N_store, K, C, ldc, part, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dd_f32(const float* R, int ldr, const float* X, int ldx, int M, int N,
                               int K, const float* E, float* C, int ldc, hipStream_t s) {
   const int G = gemm_error_parts(M, N, 0);
-  gemm_f32_kernel<EPI_DD, 1><<<G, 256, 0, s>>>(R, ldr, X, ldx, M, N, N, K, C, ldc, nullptr, E, nullptr, nullptr);
+  (f32_tile(M, N) == 32 ? gemm_f32_kernel<EPI_DD, 1, 32> : gemm_f32_kernel<EPI_DD, 1, 64>)<<<G, 256, 0, s>>>(
+      R, ldr, X, ldx, M, N, N, K, C, ldc, nullptr, E, nullptr, nullptr);
   return hipGetLastError();
 }
 

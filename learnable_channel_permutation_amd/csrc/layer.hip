@@ -3,28 +3,46 @@
 // bf16 layers, the transposed activations Xt [cin][pitch] that the backward
 // GEMM reads with the token index contiguous.
 //
-// Both kernels walk one strip of 64 channels down all T tokens, so each
-// column's sum of squares is accumulated by fixed lanes in a fixed order
+// Both kernels walk strips of channels down all T tokens, so each column's
+// sum of squares is accumulated by fixed lanes in a fixed order
 // (deterministic, no atomics).
 #include "common.h"
 #include "kernels.h"
 
 namespace lcp {
 
-__global__ __launch_bounds__(256) void colnorm_f32_kernel(const float* __restrict__ X, int T,
-                                                          int cin, float* __restrict__ norms) {
-  __shared__ float part[4][64];
+// fp32: 16 row groups of 64 channels per workgroup; row group g sums rows
+// g, g + 16, ... with four loads in flight, and the 16 group sums are added
+// in a fixed order.
+__global__ __launch_bounds__(1024) void colnorm_f32_kernel(const float* __restrict__ X, int T,
+                                                           int cin, float* __restrict__ norms) {
+  __shared__ float part[16][64];
   const int t = threadIdx.x, col = t & 63, rg = t >> 6;
   const int c = blockIdx.x * 64 + col;
   float s = 0.f;
-  if (c < cin)
-    for (int r = rg; r < T; r += 4) {
+  if (c < cin) {
+    int r = rg;
+    for (; r + 48 < T; r += 64) {
+      const float v0 = X[(size_t)r * cin + c], v1 = X[(size_t)(r + 16) * cin + c];
+      const float v2 = X[(size_t)(r + 32) * cin + c], v3 = X[(size_t)(r + 48) * cin + c];
+      s += v0 * v0;
+      s += v1 * v1;
+      s += v2 * v2;
+      s += v3 * v3;
+    }
+    for (; r < T; r += 16) {
       const float v = X[(size_t)r * cin + c];
       s += v * v;
     }
+  }
   part[rg][col] = s;
   __syncthreads();
-  if (rg == 0 && c < cin) norms[c] = sqrtf((part[0][col] + part[1][col]) + (part[2][col] + part[3][col]));
+  if (rg == 0 && c < cin) {
+    float tot = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) tot += part[g][col];
+    norms[c] = sqrtf(tot);
+  }
 }
 
 // bf16: one workgroup per strip of 32 channels, 4 waves; consecutive strips
@@ -123,7 +141,7 @@ __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __
 }
 
 hipError_t launch_colnorm_f32(const float* X, int T, int cin, float* norms, hipStream_t s) {
-  colnorm_f32_kernel<<<(cin + 63) / 64, 256, 0, s>>>(X, T, cin, norms);
+  colnorm_f32_kernel<<<(cin + 63) / 64, 1024, 0, s>>>(X, T, cin, norms);
   return hipGetLastError();
 }
 
