@@ -211,7 +211,7 @@ def run_deploy(args, torch, lcp, lcp_synth):
     """Deploy workload: Y = gather(X) Ws^T with the 2:4 packed weight, on the
     bench layer's shape (weight 4096 x 11008, 2048 tokens, B = 64)."""
     L = lcp._lib
-    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     cout, cin, T, B = spec.cout, spec.cin, spec.T, spec.B
     lay = lcp_synth.make_layer(spec)
     dev = torch.device("cuda:0")

@@ -71,7 +71,10 @@ CONFIGS = [
               64, 5, 1.0, 2, 4, True),
 ]
 
-BENCH_CONFIG = 2  # the 4096 x 11008 down_proj layer, forward + backward
+# the same layers by name
+F32_256x256, Q_PROJ_4096x4096, DOWN_PROJ_4096x11008, UP_PROJ_13824x5120, UP_PROJ_28672x8192 = CONFIGS
+
+BENCH_CONFIG = CONFIGS.index(DOWN_PROJ_4096x11008)  # forward + backward, the measured layer
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

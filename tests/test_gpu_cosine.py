@@ -110,7 +110,7 @@ def test_step_mask_ste(ci, cout, cin, T, loss, harden):
 
 def test_cosine_zero_outputs():
     """X = 0: both output norms vanish, the loss is 1 and the gradient 0."""
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=64, cin=128, T=64)
     lay.X[:] = 0.0
     say("cosine zero X")
@@ -126,7 +126,7 @@ def test_cosine_zero_outputs():
 def test_cosine_scale_invariance():
     """Scaling X by a power of two scales Y and Y~ alike: the GPU's cosine
     loss is unchanged (within rounding)."""
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=256, cin=256, T=128)
     say("cosine scale invariance")
     vals = []
@@ -143,7 +143,7 @@ def test_step_cosine_full_size_bench_layer():
     """The 4096 x 11008 layer at full size with the cosine objective and the
     mask's straight-through term: loss, mask and gradient against the full
     float64 oracle."""
-    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec)
     say("step cosine full size", spec.name)
     _check(lay, spec, lay.logits, "cosine", True, False)
@@ -152,7 +152,7 @@ def test_step_cosine_full_size_bench_layer():
 def test_step_cosine_ste_hardened_full_size_b128():
     """The 13824 x 5120 layer (B = 128, 4:8) at full size with every option:
     hardened forward, cosine objective, the mask's straight-through term."""
-    spec = lcp_synth.CONFIGS[3]
+    spec = lcp_synth.UP_PROJ_13824x5120
     lay = lcp_synth.make_layer(spec)
     lg, _ = lcp_synth.planted_logits(650, lay.cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
     say("step cosine ste hardened full size", spec.name)
@@ -164,7 +164,7 @@ def test_training_cosine_beats_wanda():
     backward through P, mask constant): the first step is plain Wanda's
     cosine loss, the loop reaches hard permutations with a lower loss, and
     the GPU's loss of the final logits agrees with the oracle's."""
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=256, cin=512, T=256)
     nb = lay.cin // spec.B
     lg0 = lcp_synth.make_logits(np.random.Generator(np.random.PCG64(7)), nb, spec.B, diag=0.5)

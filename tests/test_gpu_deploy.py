@@ -142,7 +142,7 @@ def test_deploy_after_hardened_step():
     """End to end on a seeded layer: the hardened step's P and mask (through
     lcp_step_fwd and lcp_harden) are packed and deployed; the output equals
     the oracle's X W_tilde^T for the oracle's own hard P and mask."""
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=512, cin=1024, T=320)
     lg, _ = lcp_synth.planted_logits(800, lay.cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
     say("deploy after hardened step")
@@ -171,7 +171,7 @@ def test_deploy_after_hardened_step():
 def test_deploy_full_size_bench_layer():
     """The 4096 x 11008 layer with 2048 tokens, the benchmark's deploy
     configuration, against the full float64 oracle."""
-    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     cout, cin, T, B = spec.cout, spec.cin, spec.T, spec.B
     W, X, P, perm, mask = _case(90, cout, cin, T, B)
     say("deploy full size", cout, cin, T)

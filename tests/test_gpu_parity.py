@@ -65,7 +65,7 @@ def test_sinkhorn_backward(B, iters, tau):
 
 # ---------------------------------------------------------------- N:M mask --
 def _mask_scores(rows, cin, seed):
-    lay = lcp_synth.make_layer(lcp_synth.CONFIGS[2], seed=seed, cout=rows, cin=cin, T=64)
+    lay = lcp_synth.make_layer(lcp_synth.DOWN_PROJ_4096x11008, seed=seed, cout=rows, cin=cin, T=64)
     fw = oracle.step_forward(lay.W, lay.X, lay.logits, 1.0, 5, 2, 4)
     S = fw["S_hat"].astype(np.float32)
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -95,7 +95,7 @@ def test_nm_mask_bit_exact(N, M):
 # ------------------------------------------------------------ layer setup --
 @pytest.mark.parametrize("T,cin", [(100, 96), (2048, 256), (64, 32)])
 def test_layer_init_bf16(T, cin):
-    lay = lcp_synth.make_layer(lcp_synth.CONFIGS[0], seed=5, cout=32, cin=cin, T=T, dtype="bf16")
+    lay = lcp_synth.make_layer(lcp_synth.F32_256x256, seed=5, cout=32, cin=cin, T=T, dtype="bf16")
     say("layer_init bf16", T, cin)
     X = up(lay.X, torch.bfloat16)
     norms = torch.empty(cin, dtype=torch.float32, device=DEV)
@@ -114,7 +114,7 @@ def test_layer_init_bf16(T, cin):
 
 
 def test_colnorm_f32():
-    lay = lcp_synth.make_layer(lcp_synth.CONFIGS[0], seed=6, cout=32, cin=96, T=77)
+    lay = lcp_synth.make_layer(lcp_synth.F32_256x256, seed=6, cout=32, cin=96, T=77)
     say("colnorm f32")
     norms = torch.empty(96, dtype=torch.float32, device=DEV)
     L.lcp_colnorm(up(lay.X), norms)
@@ -299,7 +299,7 @@ def test_step_tiny_shapes(ci, cout, cin, T):
 
 def test_step_c1_fp32_full_size():
     """The 256 x 256 float32 layer at its full size, forward and backward."""
-    spec = lcp_synth.CONFIGS[0]
+    spec = lcp_synth.F32_256x256
     lay = lcp_synth.make_layer(spec)
     say("step C1 f32 full")
     got = _run_step(lay, spec, backward=True)
@@ -307,7 +307,7 @@ def test_step_c1_fp32_full_size():
 
 
 def test_step_random_logits_and_harder_tau():
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=200, cin=256, T=100)
     lay.logits[:] = lcp_synth.random_logits(77, 4, 64, scale=1.0)
     spec2 = lcp_synth.LayerSpec(**{**spec.__dict__, "tau": 0.5, "iters": 7})
@@ -317,7 +317,7 @@ def test_step_random_logits_and_harder_tau():
 
 
 def test_step_zero_error_gives_zero_gradient():
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=64, cin=128, T=64)
     lay.X[:] = 0.0
     say("step zero X")
@@ -330,7 +330,7 @@ def test_step_peaked_logits_is_hard_pruning():
     """Sharply peaked logits make P a hard permutation: D = W with the pruned
     entries only, so E equals the error of plain N:M pruning of the gathered
     channels (oracle with the hard P)."""
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=128, cin=128, T=64)
     rng = np.random.Generator(np.random.PCG64(9))
     Pi = np.zeros((2, 64, 64))
@@ -345,7 +345,7 @@ def test_step_peaked_logits_is_hard_pruning():
 
 
 def test_step_deterministic():
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=384, cin=256, T=128)
     say("step determinism")
     a = _run_step(lay, spec)
@@ -358,7 +358,7 @@ def test_step_full_size_bench_layer():
     """The 4096 x 11008 layer at full size, in the launch configuration the
     benchmark times: P, every mask bit, E and the gradient against the full
     float64 oracle."""
-    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec)
     say("step full size", spec.name)
     got = _run_step(lay, spec)
@@ -461,7 +461,7 @@ def test_step_hardened_full_size_bench_layer():
     """The hardened step (Method 2 forward, straight-through backward) on the
     full 4096 x 11008 layer against the full float64 oracle: the hard P
     exactly, the mask, E and the gradient."""
-    spec = lcp_synth.CONFIGS[lcp_synth.BENCH_CONFIG]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec)
     lg, _ = lcp_synth.planted_logits(550, lay.cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
     say("step hardened full size", spec.name)
@@ -509,7 +509,7 @@ def test_adamw_kernel():
 def test_step_bwd_adamw_fused(harden):
     """The AdamW update fused into the Sinkhorn adjoint equals the plain
     backward followed by the standalone AdamW kernel, bit for bit."""
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=300, cin=512, T=160)
     say("step bwd adamw", harden)
     s = lcp.LayerSession(up(lay.W, torch.bfloat16), up(lay.X, torch.bfloat16), spec.B, spec.iters, spec.tau,
@@ -539,7 +539,7 @@ def test_training_beats_wanda():
     first step is plain Wanda (identity permutation), the loop reaches hard
     permutations with lower output error, and the GPU's error of the final
     logits agrees with the oracle's."""
-    spec = lcp_synth.CONFIGS[2]
+    spec = lcp_synth.DOWN_PROJ_4096x11008
     lay = lcp_synth.make_layer(spec, cout=256, cin=512, T=256)
     nb = lay.cin // spec.B
     lg0 = lcp_synth.make_logits(np.random.Generator(np.random.PCG64(7)), nb, spec.B, diag=0.5)
