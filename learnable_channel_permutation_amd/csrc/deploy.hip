@@ -21,6 +21,8 @@
 // that of the dense 32x32 MFMA (lane (h, n), register r: row
 // 8 (r/4) + 4h + r%4, column n). With remap_row on the A rows, register r of
 // lane (h, n) is output row 16h + r of the fragment.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -108,20 +110,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
 }
 
 // ---- 2:4 sparse GEMM ----------------------------------------------------------------
-// Y[t][o] = sum_k Ws[o][k] Xp[t][k]. 256 (rows o) x 128 (tokens t) tiles, 128
-// positions of K per stage, 8 waves in a 4 x 2 layout (each wave 64 x 64: 2 x 2
-// sparse MFMA blocks). A stage holds the 32 weight fragments of the tile
-// (32 KB, lane order, linear LDS reads), their position words (4 KB) and two
-// 128 x 64 activation sub-tiles (32 KB, rows swizzled as in the dense GEMM),
-// all moved with direct-to-LDS loads; two stages, one barrier per stage. The
-// kernel is bound by the rate at which a CU can pull tiles from L2 into LDS
-// (about 20 bytes per clock): 256 x 128 tiles minimise the bytes per useful
-// flop for one tile per CU, and 128 positions per stage halve the barriers of
-// a 64-position step.
-constexpr int SP_BM = 256, SP_BN = 128, SP_S = 2, SP_KK = 2, SP_NT = 512;
+// Y[t][o] = sum_k Ws[o][k] Xp[t][k]. 256 (rows o) x 128 (tokens t) tiles, 8
+// waves in a 4 x 2 layout (each wave 64 x 64: 2 x 2 sparse MFMA blocks), K
+// steps of 64 positions. A ring stage holds the 16 weight fragments of one
+// step (16 KB, lane order, linear LDS reads), their position words (2 KB)
+// and the 128 x 64 activation tile (16 KB, rows swizzled as in the dense
+// GEMM), all moved with direct-to-LDS loads; four stages (136 KB of LDS)
+// keep three tiles in flight per CU. The ring is software-pipelined
+// like the dense error GEMM: the five loads of tile kt + RS - 1 go out one at a
+// time between the first sub-step's MFMAs of step kt (a burst right after the
+// barrier stalls every wave on the vector-memory queue), and each step's
+// barrier sits before its second 32-position sub-step, whose MFMAs run from
+// registers while the first fragments of the next stage are read.
+constexpr int SP_BM = 256, SP_BN = 128, SP_NT = 512, SP_RS = 4, SP_NL = 5;
 constexpr int SP_A1 = (SP_BM / 32) * 2 * 1024, SP_M1 = (SP_BM / 32) * 256, SP_B1 = SP_BN * 64 * 2;
-constexpr int SP_STAGE = SP_KK * (SP_A1 + SP_M1 + SP_B1);
-constexpr int SP_MOFF = SP_KK * SP_A1, SP_BOFF = SP_KK * (SP_A1 + SP_M1);
+constexpr int SP_STAGE = SP_A1 + SP_M1 + SP_B1;
+constexpr int SP_MOFF = SP_A1, SP_BOFF = SP_A1 + SP_M1;
 
 __device__ __forceinline__ void sp_tile_coords(int g, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
   // consecutive workgroups of one XCD (id mod 8) take a compact group of
@@ -139,11 +143,19 @@ __device__ __forceinline__ void sp_tile_coords(int g, int G, int tiles_m, int ti
 
 __device__ __forceinline__ int sp_swz(int row, int ch) { return row * 64 + ((ch ^ ((row >> 1) & 7)) << 3); }
 
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited on)
+template <int N>
+__device__ __forceinline__ void sp_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int RS>
 __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restrict__ vals,
                                                           const uint32_t* __restrict__ meta,
                                                           const uint16_t* __restrict__ Xp, int T, int cout,
                                                           int cin, uint16_t* __restrict__ Y) {
-  constexpr int FM = 2, FN = 2, WM = 64, WN = 64, KK = SP_KK;
+  constexpr int FM = 2, FN = 2, NM = FM * FN, WM = 64, WN = 64, NL = SP_NL;
+  static_assert(RS >= 3 && (RS - 2) * NL < 64, "ring depth");
   extern __shared__ __attribute__((aligned(16))) unsigned char sp_lds[];
   const int tiles_m = (cout + SP_BM - 1) / SP_BM, tiles_n = (T + SP_BN - 1) / SP_BN;
   int tm, tn;
@@ -152,37 +164,29 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int h = l >> 5, ln = l & 31;
-  const int KF = cin / 32, KT = (cin + 63) / 64, RG = cout / 32;
-  const int NKS = (cin + 64 * KK - 1) / (64 * KK);
+  const int KF = cin / 32, NK = (cin + 63) / 64, RG = cout / 32;
 
-  // stage ks: weight fragments f = rgl * 2KK + kh (row group rgl, 32-position
-  // fragment kh of the stage), position words [rgl][kk], activation sub-tile kk
-  auto issue = [&](int stage, int ks) {
+  // load o of this thread for K step ks into ring stage `stage`: o < 2 the
+  // weight fragment f = 8 o + w (row group f / 2, 32-position half f % 2),
+  // o = 2 the position words of row group w, o > 2 activation chunks
+  auto issue_one = [&](int stage, int ks, int o) {
     unsigned char* sb = sp_lds + stage * SP_STAGE;
-#pragma unroll
-    for (int q = 0; q < 2 * KK; ++q) {
-      const int f = 8 * q + w, rgl = f / (2 * KK), kh = f % (2 * KK);
-      const int rg = m0 / 32 + rgl, kf = ks * 2 * KK + kh;
+    if (o < 2) {
+      const int f = 8 * o + w, rg = m0 / 32 + (f >> 1), kf = 2 * ks + (f & 1);
       const void* src = (rg < RG && kf < KF) ? (const void*)(vals + ((size_t)rg * KF + kf) * 64 + l)
                                              : (const void*)g_dep_zero;
       __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + f * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < KK; ++q) {
-      const int rg = m0 / 32 + w, kd = ks * KK + q;
-      const void* src = (rg < RG && kd < KT) ? (const void*)(meta + ((size_t)rg * KT + kd) * 64 + l)
+    } else if (o == 2) {
+      const int rg = m0 / 32 + w;
+      const void* src = (rg < RG && ks < NK) ? (const void*)(meta + ((size_t)rg * NK + ks) * 64 + l)
                                              : (const void*)g_dep_zero;
-      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_MOFF + (w * KK + q) * 256), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_MOFF + w * 256), 4, 0, 0);
+    } else {
+      const int c = ((o - 3) * 8 + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+      const int gn = n0 + row, gk = ks * 64 + ch * 8;
+      const void* src = (gn < T && gk < cin) ? (const void*)(Xp + (size_t)gn * cin + gk) : (const void*)g_dep_zero;
+      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_BOFF + ((o - 3) * 8 + w) * 1024), 16, 0, 0);
     }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c = (q * 8 + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
-        const int gn = n0 + row, gk = (ks * KK + kk) * 64 + ch * 8;
-        const void* src = (gn < T && gk < cin) ? (const void*)(Xp + (size_t)gn * cin + gk) : (const void*)g_dep_zero;
-        __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_BOFF + kk * SP_B1 + (q * 8 + w) * 1024), 16, 0, 0);
-      }
   };
 
   floatx16 acc[FM][FN];
@@ -191,51 +195,85 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
-  auto compute = [&](int stage) {
+  // fragments of 32-position sub-step p of a stage into register set p; the
+  // position word is kept whole (sub-step p uses its half p), so nothing
+  // waits for the LDS reads before the MFMAs
+  u32x4 fa[2][FM];
+  bf16x16 fb[2][FN];
+  uint32_t fm[2][FM];
+  auto rd = [&](int stage, int p) {
     const unsigned char* sb = sp_lds + stage * SP_STAGE;
     const u32x4* LA = reinterpret_cast<const u32x4*>(sb);
     const uint32_t* LM = reinterpret_cast<const uint32_t*>(sb + SP_MOFF);
+    const uint16_t* LB = reinterpret_cast<const uint16_t*>(sb + SP_BOFF);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint16_t* LB = reinterpret_cast<const uint16_t*>(sb + SP_BOFF + kk * SP_B1);
-      uint32_t mw[FM];
+    for (int i = 0; i < FM; ++i) {
+      fa[p][i] = LA[((wm * FM + i) * 2 + p) * 64 + l];
+      fm[p][i] = LM[(wm * FM + i) * 64 + l];
+    }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) mw[i] = LM[((wm * FM + i) * KK + kk) * 64 + l];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        u32x4 a[FM];
-        bf16x16 bv[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) a[i] = LA[((wm * FM + i) * 2 * KK + 2 * kk + p) * 64 + l];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wn * WN + 32 * j + ln;
-          const u32x4 b0 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + h)]);
-          const u32x4 b1 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + 2 + h)]);
-          typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-          bv[j] = __builtin_bit_cast(bf16x16, u32x8{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w});
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int idx = (int)((mw[i] >> (16 * p)) & 0xffffu);
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(a[i]), bv[j], acc[i][j], idx, 0, 0);
-        }
-      }
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * WN + 32 * j + ln;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + h)]);
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + 2 + h)]);
+      typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+      fb[p][j] = __builtin_bit_cast(bf16x16, u32x8{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w});
     }
   };
-
-  // two stages: stage ks + 1 is loaded while stage ks is multiplied; the
-  // wait retires this thread's loads of stage ks, the barrier everyone's, and
-  // also the reads of the stage that is refilled next
-  if (NKS > 0) issue(0, 0);
-  for (int ks = 0; ks < NKS; ++ks) {
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  auto mma = [&](int p, int m) {
+    const int i = m / FN, j = m % FN;
+    const int idx = (int)((fm[p][i] >> (16 * p)) & 0xffffu);
+    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(fa[p][i]), fb[p][j], acc[i][j], idx, 0, 0);
+  };
+  // step on stage `stage` (sub-step 0 fragments already in registers): with `load`
+  // the tile of K step ks goes to stage `lstage`; with `next` the first
+  // fragments of stage `nstage` are read after the barrier. WAIT (steady
+  // state): the loads of the RS - 2 tiles after the next one may stay in flight.
+  auto step = [&](int stage, int lstage, int ks, int nstage, bool load, bool next, auto WAIT) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // sub-step 0's fragments are in
+    __builtin_amdgcn_sched_barrier(0);
+    rd(stage, 1);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int o = 0; o < NL; ++o)
+        if (load && o * NM / NL == m) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_one(lstage, ks, o);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      mma(0, m);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(WAIT)::value) sp_wait_vmcnt<(RS - 2) * NL>();
+    else sp_wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    if (ks + 1 < NKS) issue((ks + 1) & 1, ks + 1);
-    compute(ks & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) rd(nstage, 0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) mma(1, m);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: tiles 0 .. RS - 2 (a tile past K reads zeros and is never multiplied)
+#pragma unroll
+  for (int s = 0; s < RS - 1; ++s)
+#pragma unroll
+    for (int o = 0; o < NL; ++o) issue_one(s, s, o);
+  sp_wait_vmcnt<(RS - 2) * NL>();
+  __builtin_amdgcn_s_barrier();
+  rd(0, 0);
+  int kt = 0;
+  for (; kt + 2 * RS - 2 < NK; kt += RS) {                 // RS steady-state steps
+#pragma unroll
+    for (int s = 0; s < RS; ++s)
+      step(s, (s + RS - 1) % RS, kt + s + RS - 1, (s + 1) % RS, true, true, std::true_type{});
   }
+  for (; kt < NK; ++kt)                                    // the last steps, all loads retired at each barrier
+    step(kt % RS, (kt + RS - 1) % RS, kt + RS - 1, (kt + 1) % RS, kt + RS - 1 < NK, kt + 1 < NK,
+         std::false_type{});
+  sp_wait_vmcnt<0>();                                      // the zero tiles of a short K
 
   // lane (h, ln) of block (i, j): token n0 + wn*64 + 32j + ln, rows
   // m0 + wm*64 + 32i + 16h + r (r < 16)
@@ -276,7 +314,7 @@ hipError_t launch_gather(const uint16_t* X, int T, int cin, int B, const int* pe
 hipError_t launch_spgemm(const u32x4* vals, const uint32_t* meta, const uint16_t* Xp, int T, int cout, int cin,
                          uint16_t* Y, hipStream_t s) {
   const int G = ((cout + SP_BM - 1) / SP_BM) * ((T + SP_BN - 1) / SP_BN);
-  spgemm_kernel<<<G, SP_NT, SP_S * SP_STAGE, s>>>(vals, meta, Xp, T, cout, cin, Y);
+  spgemm_kernel<SP_RS><<<G, SP_NT, SP_RS * SP_STAGE, s>>>(vals, meta, Xp, T, cout, cin, Y);
   return hipGetLastError();
 }
 
