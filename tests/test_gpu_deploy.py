@@ -179,3 +179,17 @@ def test_deploy_full_size_bench_layer():
     Yg = _deploy(W, X, perm, bits, B)
     ref = oracle.deploy_forward(W, X, P, mask)
     _check_y(Yg, ref, np.abs(W), np.abs(X))
+
+
+@pytest.mark.parametrize("cin", [32, 96, 224, 416, 480, 736, 992])
+def test_deploy_forward_k_tails(cin):
+    """Every count of 64-position steps modulo the ring depth, short K
+    (fewer steps than the ring holds) and odd fragment counts (cin % 64 ==
+    32), with a ragged token tail and a partial row tile."""
+    cout, T, B = 288, 130, 32
+    W, X, P, perm, mask = _case(90 + cin, cout, cin, T, B)
+    say("deploy forward k tails", cout, cin, T, B)
+    bits = torch.from_numpy(oracle.pack_bits(mask).view(np.int32)).to(DEV)
+    Yg = _deploy(W, X, perm, bits, B)
+    ref = oracle.deploy_forward(W, X, P, mask)
+    _check_y(Yg, ref, np.abs(W), np.abs(X))
