@@ -18,9 +18,9 @@
 // stored); out-of-range K chunks and B rows read a 16-byte zero block, so
 // padded output columns come out exactly zero.
 //  * gemm_dd_kernel (the backward product): a two-stage ring on 32x32x16
-//    MFMAs, one barrier per K step after which the next tile's loads are
-//    issued; inside a step the MFMAs of one 16-wide sub-step are interleaved
-//    one-to-one with the fragment reads of the next (sched_group_barrier).
+//    MFMAs, one barrier per K step after which the next tile's loads go out
+//    one at a time between the MFMAs of the first sub-steps; each 16-wide
+//    sub-step reads the next one's fragments before its MFMAs.
 //  * gemm_err_kernel (the error product): a software-pipelined three-stage
 //    ring on 16x16x32 MFMAs, described at the kernel.
 //
@@ -59,27 +59,6 @@ __device__ __forceinline__ void tile_coords(int g, int G, int tiles_m, int tiles
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 1) & 7)) << 3); }
 
-// Pin the order of one K step: the first sub-step's fragment reads, then for
-// every sub-step its MFMAs interleaved with the next sub-step's reads.
-template <int FM, int FN>
-__device__ __forceinline__ void pin_schedule() {
-  constexpr int NR = FM + FN, NM = FM * FN;
-  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-  for (int p = 0; p < GBK / 16; ++p) {
-    if (p + 1 < GBK / 16) {
-#pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-    }
-  }
-}
-
 template <int BM, int BN, int S>
 constexpr size_t gemm_lds_bytes() { return (size_t)S * (BM + BN) * GBK * 2; }
 
@@ -90,7 +69,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // The backward product C = coef[1] * A B^T (bf16 out).
-template <int BM, int BN, int S>
+template <int BM, int BN, int S, int LSP>
 __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M,
     int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, const float* __restrict__ Eptr) {
@@ -107,23 +86,22 @@ __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
   const int wm = w / GWN, wn = w % GWN;
   const int h = l >> 5, ln = l & 31;
 
-  // load instruction q of wave w fills the 64 consecutive 16-byte chunks
-  // (q * GNW + w) * 64 + lane of the stage
-  auto issue = [&](int stage, int k0) {
+  // load q (< AI: A rows, else B rows) of wave w fills the 64 consecutive
+  // 16-byte chunks (q' * GNW + w) * 64 + lane of its matrix in the stage
+  constexpr int NL = AI + BI;                              // load instructions per tile
+  auto issue_one = [&](int stage, int k0, int q) {
     uint16_t* sb = lds + stage * STAGE;
-#pragma unroll
-    for (int q = 0; q < AI; ++q) {
+    if (q < AI) {
       const int c = (q * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
       const int gm = min(m0 + row, M - 1), gk = k0 + ch * 8;
       const void* src = (gk < K) ? (const void*)(A + (size_t)gm * lda + gk) : (const void*)g_zero16;
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + (q * GNW + w) * 64 * 8), 16, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < BI; ++q) {
-      const int c = (q * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+    } else {
+      const int qb = q - AI;
+      const int c = (qb * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
       const int gn = n0 + row, gk = k0 + ch * 8;
       const void* src = (gk < K && gn < N_valid) ? (const void*)(Bm + (size_t)gn * ldb + gk) : (const void*)g_zero16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + BM * GBK + (q * GNW + w) * 64 * 8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + BM * GBK + (qb * GNW + w) * 64 * 8), 16, 0, 0);
     }
   };
 
@@ -138,7 +116,10 @@ __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
 #pragma unroll
   for (int j = 0; j < FN; ++j) brow[j] = wn * WN + j * 32 + remap_row(ln);
 
-  auto compute = [&](int stage) {
+  // multiply the tile in `stage`; with `load` the tile at k0 goes to stage
+  // `lstage`, one load between consecutive MFMAs of the first LSP sub-steps
+  constexpr int NP = GBK / 16, NM = FM * FN, SLOTS = LSP * NM;
+  auto compute = [&](int stage, int lstage, int k0, auto LOAD) {
     const uint16_t* As = lds + stage * STAGE;
     const uint16_t* Bs = As + BM * GBK;
     u32x4 fa[2][FM], fb[2][FN];
@@ -147,40 +128,47 @@ __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[0][j] = *reinterpret_cast<const u32x4*>(&Bs[swz(brow[j], h)]);
 #pragma unroll
-    for (int p = 0; p < GBK / 16; ++p) {
+    for (int p = 0; p < NP; ++p) {
       const int c = p & 1;
-      if (p + 1 < GBK / 16) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (p + 1 < NP) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[c ^ 1][i] = *reinterpret_cast<const u32x4*>(&As[swz(arow[i], 2 * (p + 1) + h)]);
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[c ^ 1][j] = *reinterpret_cast<const u32x4*>(&Bs[swz(brow[j], 2 * (p + 1) + h)]);
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int m = 0; m < NM; ++m) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[c][j], fa[c][i], acc[i][j]);
+        for (int o = 0; o < NL; ++o)
+          if (decltype(LOAD)::value && p < LSP && o * SLOTS / NL == p * NM + m) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(lstage, k0, o);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        const int i = m / FN, j = m % FN;
+        acc[i][j] = mfma32(fb[c][j], fa[c][i], acc[i][j]);
+      }
     }
-    pin_schedule<FM, FN>();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // S-stage ring: tiles kt + 1 .. kt + S - 2 stay in flight while tile kt is
-  // multiplied. At step kt this thread waits until only the loads issued for
-  // later tiles are outstanding (its part of tile kt has landed); the barrier
-  // then makes every thread's part visible and guarantees that the stage of
-  // tile kt - 1 is no longer read before it is refilled with tile kt + S - 1.
+  // two-stage ring: at step kt this thread waits for its loads of tile kt,
+  // the barrier makes every thread's part visible and guarantees that the
+  // stage of tile kt - 1 is no longer read; tile kt + 1 then goes there while
+  // tile kt is multiplied.
+  static_assert(S == 2, "two stages");
   const int nk = (K + GBK - 1) / GBK;
-  constexpr int NL = AI + BI;                              // load instructions per tile
-  static_assert(S == 2 || S == 3, "two or three stages");
 #pragma unroll
-  for (int q = 0; q < S - 1; ++q)
-    if (q < nk) issue(q, q * GBK);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (S == 3 && kt + 1 < nk) wait_vmcnt<NL>();
-    else wait_vmcnt<0>();
+  for (int q = 0; q < NL; ++q) issue_one(0, 0, q);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * GBK);
-    compute(kt % S);
+    compute(kt & 1, (kt + 1) & 1, (kt + 1) * GBK, std::true_type{});
   }
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  compute((nk - 1) & 1, 0, 0, std::false_type{});
 
   // ---- epilogue: lane (h, ln) of block (i, j) holds row m0 + wm*WM + 32i + ln,
   // columns n0 + wn*WN + 32j + 16h + r, r < 16.
@@ -590,6 +578,7 @@ __global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restr
 // tiles, two stages (128 KB).
 constexpr int EBM = 256, EBN = 128, DBM = 256, DBN = 256, DS = 2;
 constexpr int EMF = 16;   // MFMA of the error GEMM
+constexpr int DLSP = 2;   // dD GEMM: sub-steps its loads are spread over
 
 // fp32 tile size: 64, or 32 when 64-wide tiles would occupy fewer than 128
 // of the 256 CUs
@@ -618,7 +607,7 @@ hipError_t launch_gemm_error_bf16(const uint16_t* A, int lda, const uint16_t* Bm
 hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
                                int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s) {
   const int G = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
-  gemm_dd_kernel<DBM, DBN, DS><<<G, GNT, gemm_lds_bytes<DBM, DBN, DS>(), s>>>(A, lda, Bm, ldb, M, N, N, K, C,
+  gemm_dd_kernel<DBM, DBN, DS, DLSP><<<G, GNT, gemm_lds_bytes<DBM, DBN, DS>(), s>>>(A, lda, Bm, ldb, M, N, N, K, C,
                                                                            ldc, E);
   return hipGetLastError();
 }
