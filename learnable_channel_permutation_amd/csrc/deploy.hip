@@ -196,8 +196,7 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
   // fragments of 32-position sub-step p of a stage into register set p; the
-  // position word is kept whole (sub-step p uses its half p), so nothing
-  // waits for the LDS reads before the MFMAs
+  // position word is kept whole (sub-step p uses its half p)
   u32x4 fa[2][FM];
   bf16x16 fb[2][FN];
   uint32_t fm[2][FM];
@@ -220,10 +219,14 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
       fb[p][j] = __builtin_bit_cast(bf16x16, u32x8{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w});
     }
   };
+  // the instruction's index-set field picks half p of the position word
   auto mma = [&](int p, int m) {
     const int i = m / FN, j = m % FN;
-    const int idx = (int)((fm[p][i] >> (16 * p)) & 0xffffu);
-    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(fa[p][i]), fb[p][j], acc[i][j], idx, 0, 0);
+    const int idx = (int)fm[p][i];
+    if (p == 0)
+      acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(fa[p][i]), fb[p][j], acc[i][j], idx, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(fa[p][i]), fb[p][j], acc[i][j], idx, 0, 1);
   };
   // step on stage `stage` (sub-step 0 fragments already in registers): with `load`
   // the tile of K step ks goes to stage `lstage`; with `next` the first
@@ -251,6 +254,7 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (next) rd(nstage, 0);
+    __builtin_amdgcn_sched_barrier(0);                     // nothing here waits for those reads
 #pragma unroll
     for (int m = 0; m < NM; ++m) mma(1, m);
     __builtin_amdgcn_sched_barrier(0);
