@@ -92,6 +92,22 @@ def test_nm_mask_bit_exact(N, M):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("rows,cin", [(1, 32), (5, 96), (300, 1056)])
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 8)])
+def test_nm_mask_shapes(rows, cin, N, M):
+    """Partial workgroups and partial waves: the last thread's words and
+    the words past the end (which must not be written)."""
+    S = np.ascontiguousarray(_mask_scores(max(rows, 8), (cin + 63) // 64 * 64, 7 + rows)[:rows, :cin])
+    say("nm_mask shapes", rows, cin, N, M)
+    flat = torch.full((rows * (cin // 32) + 16,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    L.lcp_nm_mask(up(S), N, M, flat)
+    torch.cuda.synchronize()
+    want = oracle.pack_bits(oracle.nm_mask(S, N, M))
+    got = flat.cpu().numpy()
+    assert np.array_equal(got[: rows * (cin // 32)].view(np.uint32).reshape(rows, cin // 32), want)
+    assert np.all(got[rows * (cin // 32):] == 0x5A5A5A5A)
+
+
 # ------------------------------------------------------------ layer setup --
 @pytest.mark.parametrize("T,cin", [(100, 96), (2048, 256), (64, 32)])
 def test_layer_init_bf16(T, cin):
