@@ -238,11 +238,15 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
           aop[2 * t + u] = u32x4{pack2(a[8 * u], a[8 * u + 1]), pack2(a[8 * u + 2], a[8 * u + 3]),
                                  pack2(a[8 * u + 4], a[8 * u + 5]), pack2(a[8 * u + 6], a[8 * u + 7])};
       }
-      // mask words, block-major: the tile's 32 rows x TT words are contiguous
+      // mask words, block-major: the tile's 32 rows x TT words are contiguous;
+      // stored non-temporally (read again only by the backward's adjoint)
       if (h == 0 && i < rows) {
         uint32_t* bw = bits + ((size_t)b * rows + i) * TT;
-        if constexpr (TT == 4) *reinterpret_cast<u32x4*>(bw) = u32x4{kw[0], kw[1], kw[2], kw[3]};
-        else if constexpr (TT == 2) *reinterpret_cast<uint2*>(bw) = uint2{kw[0], kw[1]};
+        if constexpr (TT == 4) __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]}, reinterpret_cast<u32x4*>(bw));
+        else if constexpr (TT == 2) {
+          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(v2u{kw[0], kw[1]}, reinterpret_cast<v2u*>(bw));
+        }
         else bw[0] = kw[0];
       }
 #pragma unroll
