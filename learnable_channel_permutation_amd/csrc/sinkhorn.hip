@@ -87,33 +87,13 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   s = a + b;
 }
 
-// One forward iteration on the register block, using reduction buffer `red`
-// (WAVES * B (max, sum) pairs; alternate two buffers between iterations) and
-// `ccb` (B column offsets).
-// Writes the row offsets of this lane's rows to roff[row] (if lc == 0) and the
-// column offsets to coff[col] (if w == 0 && lr == 0); either may be null.
+// Column step of one iteration from the values themselves: Z = U - lse_col(U)
+// with each wave's (max, sum) pairs over its 16 rows merged in LDS.
 template <int B>
-__device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* red, float* ccb, float* roff,
-                                        float* coff, int w, int lr, int lc) {
+__device__ __forceinline__ void col_step_exact(float (&z)[4][SkGeom<B>::CPL], float2* red, float* ccb, int w,
+                                               int lr, int lc) {
   constexpr int CPL = SkGeom<B>::CPL;
   constexpr int WAVES = SkGeom<B>::WAVES;
-  // ---- row step: U = Z - lse_row(Z)
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    float m = z[a][0];
-#pragma unroll
-    for (int c = 1; c < CPL; ++c) m = fmaxf(m, z[a][c]);
-    m = row16_max(m);
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) s += exp2_(z[a][c] - m);
-    s = row16_sum(s);
-    const float r = m + log2_(s);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) z[a][c] -= r;
-    if (roff != nullptr && lc == 0) roff[16 * w + 4 * lr + a] = r;
-  }
-  // ---- column step: Z = U - lse_col(U); each wave's (max, sum) over its 16 rows
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     float m = fmaxf(fmaxf(z[0][c], z[1][c]), fmaxf(z[2][c], z[3][c]));
@@ -138,6 +118,69 @@ __device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* r
     if (lr == 0) ccb[col] = m + log2_(s);
   }
   __syncthreads();
+}
+
+// One forward iteration on the register block, using reduction buffer `red`
+// (WAVES * B (max, sum) pairs; alternate two buffers between iterations),
+// `ccb` (B column offsets) and the flag word `flag` (alternate two as well).
+// The row step keeps its exponentials: exp2(U) = exp2(Z - rowmax) / rowsum,
+// so the column sums of exp2(U) need no second exponential. A column whose
+// sum falls below 2^-90 (its terms may have underflowed in the row step)
+// sends the whole block through the exact log-domain column step instead.
+// Writes the row offsets of this lane's rows to roff[row] (if lc == 0) and the
+// column offsets to coff[col] (if w == 0 && lr == 0); either may be null.
+template <int B>
+__device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* red, float* ccb, int* flag,
+                                        float* roff, float* coff, int w, int lr, int lc) {
+  constexpr int CPL = SkGeom<B>::CPL;
+  constexpr int WAVES = SkGeom<B>::WAVES;
+  // ---- row step: U = Z - lse_row(Z), q = exp2(U)
+  float q[4][CPL];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    float m = z[a][0];
+#pragma unroll
+    for (int c = 1; c < CPL; ++c) m = fmaxf(m, z[a][c]);
+    m = row16_max(m);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      q[a][c] = exp2_(z[a][c] - m);
+      s += q[a][c];
+    }
+    s = row16_sum(s);
+    const float r = m + log2_(s);
+    const float inv = 1.f / s;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      z[a][c] -= r;
+      q[a][c] *= inv;
+    }
+    if (roff != nullptr && lc == 0) roff[16 * w + 4 * lr + a] = r;
+  }
+  // ---- column step: Z = U - log2(colsum(q)); each wave's sums over its 16 rows
+  if (w == 0 && lr == 0 && lc == 0) *flag = 0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    float s = (q[0][c] + q[1][c]) + (q[2][c] + q[3][c]);
+    s = xor32_sum(xor16_sum(s));
+    if (lr == 0) red[w * B + lc * CPL + c] = float2{s, 0.f};
+  }
+  __syncthreads();
+  {
+    const int l = 16 * lr + lc, col = 16 * w + lc;
+    float s = 0.f;
+#pragma unroll
+    for (int v = lr; v < WAVES; v += 4) s += red[v * B + col].x;
+    s += partner16(s, l);
+    s += partner32(s, l);
+    if (lr == 0) {
+      ccb[col] = log2_(s);
+      if (!(s >= 0x1p-90f)) *flag = 1;
+    }
+  }
+  __syncthreads();
+  if (*flag != 0) col_step_exact<B>(z, red, ccb, w, lr, lc);   // block-uniform
   float cv[CPL];
   ld_cols<CPL>(ccb + lc * CPL, cv);
 #pragma unroll
@@ -160,6 +203,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
   constexpr int PP = B + 2;                       // LDS row pitch of the staged block
   __shared__ float2 red[2][WAVES * B];
   __shared__ __attribute__((aligned(16))) float ccb[B];
+  __shared__ int skflag[2];
   extern __shared__ float ps[];                   // [B][PP] P block, then [B] norms
   const int b = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l >> 4, lc = l & 15;
@@ -172,7 +216,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
   for (int it = 0; it < iters; ++it) {
     float* ro = off ? off + ((size_t)(b * iters + it) * 2 + 0) * B : nullptr;
     float* co = off ? off + ((size_t)(b * iters + it) * 2 + 1) * B : nullptr;
-    sk_iter<B>(z, red[it & 1], ccb, ro, co, w, lr, lc);
+    sk_iter<B>(z, red[it & 1], ccb, &skflag[it & 1], ro, co, w, lr, lc);
   }
   float* dst = P + (size_t)b * B * B;
 #pragma unroll
@@ -218,6 +262,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
   __shared__ float2 red[2][WAVES * B];
   __shared__ float red_g[2][WAVES * B];
   __shared__ __attribute__((aligned(16))) float ccb[B];
+  __shared__ int skflag[2];
   const int b = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l >> 4, lc = l & 15;
   const int row0 = 16 * w + 4 * lr;          // this lane's rows row0 .. row0 + 3
@@ -269,7 +314,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
 #pragma unroll
       for (int c = 0; c < CPL; ++c) z[a][c] = z0[a][c];
     for (int it = 0; it < iters; ++it)
-      sk_iter<B>(z, red[it & 1], ccb, sh_off + (2 * it) * B, sh_off + (2 * it + 1) * B, w, lr, lc);
+      sk_iter<B>(z, red[it & 1], ccb, &skflag[it & 1], sh_off + (2 * it) * B, sh_off + (2 * it + 1) * B, w, lr, lc);
   }
   __syncthreads();
 

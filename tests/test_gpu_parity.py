@@ -48,6 +48,41 @@ def test_sinkhorn_forward(B, iters, tau, kind):
     assert np.array_equal(down(d_lg), got)
 
 
+@pytest.mark.parametrize("B", [32, 64, 128])
+def test_sinkhorn_underflowing_columns(B):
+    """Blocks with a column far below every row's maximum (its exponentials
+    underflow in the row step) next to ordinary blocks: the forward, and the
+    backward that recomputes the iterates, still follow the log-domain
+    definition. Logits of magnitude 200 put |Z| near 290 (base 2), which
+    float32 carries to about |Z| 2^-24 per operation; over the 2L
+    subtractions of the iterates that bounds P's relative error by
+    2L |Z| 2^-24 ln 2 (1.2e-4 here) on top of the usual 1e-5."""
+    nb, iters, tau = 6, 5, 1.0
+    lg = lcp_synth.random_logits(300 + B, nb, B, scale=0.5)
+    lg[0, :, 3] = -200.0                  # one such column
+    lg[1, :, :B // 2] -= 150.0            # half the columns of a block
+    lg[2, 5, :] = 120.0                   # one dominant row
+    lg[2, 5, 7] = 240.0
+    say("sinkhorn underflowing columns", B)
+    d_lg = up(lg)
+    d_P = torch.empty_like(d_lg)
+    L.lcp_sinkhorn(d_lg, d_P, iters, tau)
+    torch.cuda.synchronize()
+    ref = oracle.sinkhorn(lg.astype(np.float64), np.float64(tau), iters)
+    got = down(d_P)
+    assert np.all(np.isfinite(got))
+    zmax = np.max(np.abs(lg)) / tau * np.log2(np.e)
+    tol = _sink_tol(ref) + 2 * iters * zmax * 2.0 ** -24 * np.log(2) * np.abs(ref)
+    assert np.all(np.abs(got - ref) <= tol), np.max(np.abs(got - ref) / (np.abs(ref) + 1e-9))
+    dP = lcp_synth.random_matrix(400 + B, (nb, B, B))
+    d_out = torch.empty((nb, B, B), dtype=torch.float32, device=DEV)
+    L.lcp_sinkhorn_bwd(d_lg, up(dP), iters, tau, d_out)
+    torch.cuda.synchronize()
+    P, tr = oracle.sinkhorn(lg.astype(np.float64), np.float64(tau), iters, trace=True)
+    want = oracle.sinkhorn_adjoint(dP.astype(np.float64), P, tr, np.float64(tau))
+    assert rel_fro(down(d_out), want) < 1e-4
+
+
 @pytest.mark.parametrize("B,iters,tau", [(32, 5, 1.0), (64, 5, 0.7), (128, 7, 1.0), (64, 1, 1.0)])
 def test_sinkhorn_backward(B, iters, tau):
     nb = 19
