@@ -12,9 +12,16 @@ Inputs are resident in HBM before the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--breakdown]
 
-Prints one JSON line. `roofline` is computed from the average duration of the
-dominant kernel, measured with HIP events recorded on the step's stream inside
-the timed region; `cpu_baseline` times the float64 oracle on the host.
+Prints one JSON line. `value` is steps/s from the median step time (an event
+at every step boundary of the K timed steps; `ms_per_step` is their mean).
+`roofline` is computed from the average duration of the dominant kernel,
+measured with HIP events recorded on the step's stream inside the timed
+region, against the published peak and (`roofline.attainable`) against
+hipBLASLt on the same GEMM shape in the same process. After the timed region
+a per-kernel pass (`kernels`: µs, algorithmic bytes or flops, GB/s or
+TFLOP/s, fractions of the published peak and of the measured copy / hipBLASLt
+rates) and the attainable probes (`attainable`) run; `cpu_baseline` times the
+float64 oracle on the host; `source` identifies the library sources.
 """
 from __future__ import annotations
 
@@ -43,7 +50,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=None, help="layer config index (default: the bench layer)")
-    ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--breakdown", action="store_true", help="also print the per-kernel times to stderr")
+    ap.add_argument("--no-kernels", action="store_true",
+                    help="skip the per-kernel pass and the attainable-peak probes after the timed region")
     ap.add_argument("--harden", action="store_true",
                     help="hardened forward + straight-through backward (another workload)")
     ap.add_argument("--cosine", action="store_true",
@@ -110,6 +119,98 @@ def measured_traffic(kernel, shape):
     if list(k.get("shape", [])) != list(shape):
         return None
     return k.get("bytes_per_launch")
+
+
+def kernel_work(spec, names):
+    """Algorithmic work of one launch of each step kernel on this layer:
+    ("bytes", n) for the HBM-bound kernels (every input read once, every
+    output written once) or ("flops", n) for the two GEMMs."""
+    cout, cin, T, B, L = spec.cout, spec.cin, spec.T, spec.B, spec.iters
+    nb = cin // B
+    es = 2 if spec.dtype == "bf16" else 4
+    pitch = (T + 63) // 64 * 64
+    KS, TT = B // 16, B // 32
+    frag = TT * KS * 64 * 16                                      # bytes of one fragment set
+    frags = nb * ((2 + (2 if B == 128 else 3)) * frag + frag) if spec.dtype == "bf16" else 0
+    wk = {
+        "layer_init": ("bytes", es * T * cin + (2 * cin * pitch if spec.dtype == "bf16" else 0) + 4 * cin),
+        "sinkhorn_fwd": ("bytes", 8 * nb * B * B + 4 * nb * L * 2 * B + 4 * cin + frags),
+        "permute_mask_unpermute": ("bytes", 2 * es * cout * cin + cout * cin // 8 + 4 * nb * B * B),
+        "error_gemm": ("flops", 2.0 * cout * cin * T),
+        "error_finalize": ("bytes", 4 * ((cout + 255) // 256) * ((pitch + 127) // 128)),
+        "dD_gemm": ("flops", 2.0 * cout * cin * T),
+        "block_adjoint": ("bytes", 2 * es * cout * cin + cout * cin // 8 + 4 * nb * B * B),
+        "sinkhorn_bwd": ("bytes", 12 * nb * B * B + 4 * nb * L * 2 * B),
+    }
+    return {n: wk[n] for n in names if n in wk}
+
+
+def attainable_peaks(torch, spec):
+    """Measured-attainable denominators on this GPU, in this process: a plain
+    device copy (torch's copy kernel, 1 GiB read + 1 GiB written) and
+    hipBLASLt (torch.matmul) on the two GEMM shapes of the step with random
+    bf16 operands. Each is the best of 3 rounds of 10 timed calls."""
+    dev = torch.device("cuda:0")
+    out = {}
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def best(fn, reps=10, rounds=3):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(rounds):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b) / reps)
+        return min(ms)
+
+    ms = best(lambda: dst.copy_(src))
+    out["copy_GB_per_s"] = round(2.0 * n * 4 / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    cout, cin, T = spec.cout, spec.cin, spec.T
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    R = torch.randn((cout, T), device=dev, generator=g).to(torch.bfloat16)
+    X = torch.randn((T, cin), device=dev, generator=g).to(torch.bfloat16)
+    D = torch.randn((cout, cin), device=dev, generator=g).to(torch.bfloat16)
+    Xt = X.t().contiguous()
+    flops = 2.0 * cout * cin * T
+    ms_dd = best(lambda: torch.matmul(R, X))
+    ms_err = best(lambda: torch.matmul(D, Xt))
+    out["hipblaslt_dD_TFLOP_per_s"] = round(flops / (ms_dd * 1e-3) / 1e12, 1)
+    out["hipblaslt_error_TFLOP_per_s"] = round(flops / (ms_err * 1e-3) / 1e12, 1)
+    out["hipblaslt_dD_us"] = round(ms_dd * 1e3, 1)
+    out["hipblaslt_error_us"] = round(ms_err * 1e3, 1)
+    del R, X, D, Xt
+    torch.cuda.synchronize()
+    return out
+
+
+def source_identity():
+    """sha256 (16 hex) of the library sources as built (code only), and the
+    git commit when the tree is a checkout."""
+    import subprocess
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "learnable_channel_permutation_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
+    sha = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        if r.returncode == 0:
+            sha = r.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    return {"csrc_sha16": h.hexdigest()[:16], "git": sha}
 
 
 class HipEvents:
@@ -436,7 +537,11 @@ def main():
             "other_gemm": {"kernel": "dD_gemm" if dom_name == "error_gemm" else "error_gemm",
                            "ms": round(bwd_gemm_ms if dom_name == "error_gemm" else fwd_gemm_ms, 4)}}
 
-    if args.breakdown:
+    kernels = None
+    if not args.no_kernels:
+        # per-kernel pass after the timed region: events around every kernel
+        # of 20 further steps (kept out of the timed steps so that the extra
+        # event records do not perturb them)
         fwd_names = FWD_NAMES[:3] + (["cosine_finalize"] if args.cosine else FWD_NAMES[3:]) \
             + (["harden"] if args.harden else [])
         bwd_names = BWD_NAMES + (["cosine_grad"] if args.cosine else [])
@@ -456,10 +561,28 @@ def main():
                                      [_Ev(evs[n][r][1]) for n in bwd_names])
                 sess.backward(logits, dlogits, timing=tb)
         torch.cuda.synchronize()
-        print("per-kernel ms (mean of %d):" % reps, file=sys.stderr)
-        print("  %-24s %8.4f" % ("layer_init", sum(a.elapsed_time(b) for a, b in init_ev) / reps), file=sys.stderr)
+        per = {"layer_init": sum(a.elapsed_time(b) for a, b in init_ev) / reps}
         for n in names:
-            print("  %-24s %8.4f" % (n, sum(he.ms(a, b) for a, b in evs[n]) / reps), file=sys.stderr)
+            per[n] = sum(he.ms(a, b) for a, b in evs[n]) / reps
+        work = kernel_work(spec, list(per))
+        kernels = {}
+        for n, kms in per.items():
+            e = {"us": round(kms * 1e3, 1)}
+            if n in work:
+                kind, amount = work[n]
+                if kind == "bytes":
+                    gbs = amount / (kms * 1e-3) / 1e9
+                    e.update({"bytes": int(amount), "GB_per_s": round(gbs, 1),
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)})
+                else:
+                    tfs = amount / (kms * 1e-3) / 1e12
+                    e.update({"flops": amount, "TFLOP_per_s": round(tfs, 1),
+                              "frac_mfma": round(tfs / PEAK_BF16_TFLOPS, 3)})
+            kernels[n] = e
+        if args.breakdown:
+            print("per-kernel ms (mean of %d):" % reps, file=sys.stderr)
+            for n, kms in per.items():
+                print("  %-24s %8.4f" % (n, kms), file=sys.stderr)
     graph = None
     if args.graph and not args.adamw:
         g = sess.capture_step(logits, dlogits, setup=True)
@@ -479,6 +602,20 @@ def main():
         print("saturating sizes: " + json.dumps(sat), file=sys.stderr)
     he.close()
 
+    attain = None
+    if not args.no_kernels and spec.dtype == "bf16":
+        attain = attainable_peaks(torch, spec)
+        gemm_att = attain["hipblaslt_dD_TFLOP_per_s"] if dom_name == "dD_gemm" else attain["hipblaslt_error_TFLOP_per_s"]
+        roof["attainable"] = {"peak": gemm_att, "unit": "TFLOP/s", "frac": round(achieved / gemm_att, 4),
+                              "source": "hipBLASLt (torch.matmul) on the same GEMM shape, same process"}
+        if kernels is not None:
+            for n, e in kernels.items():
+                if "GB_per_s" in e:
+                    e["frac_copy"] = round(e["GB_per_s"] / attain["copy_GB_per_s"], 3)
+                elif "TFLOP_per_s" in e:
+                    ref = attain["hipblaslt_dD_TFLOP_per_s"] if n == "dD_gemm" else attain["hipblaslt_error_TFLOP_per_s"]
+                    e["frac_hipblaslt"] = round(e["TFLOP_per_s"] / ref, 3)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, lay, hard=args.harden, loss=loss, mask_ste=args.mask_ste)
@@ -486,13 +623,15 @@ def main():
     out = {
         "metric": "LCP %s steps/sec per layer (%dx%d, %d:%d)" % ("fwd+bwd" if spec.backward else "fwd",
                                                                  spec.cout, spec.cin, spec.N, spec.M),
-        "value": round(1000.0 / ms, 2),
+        "value": round(1000.0 / ms_median, 2),
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_median": round(ms_median, 4),
+        "value_from": "median step time (event at every step boundary); ms_per_step is the mean over the K steps",
+        "value_mean": round(1000.0 / ms, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -508,7 +647,10 @@ def main():
                    "N": spec.N, "M": spec.M, "backward": spec.backward, "objective": loss,
                    "includes_layer_setup": True},
         "roofline": roof,
+        "kernels": kernels,
+        "attainable": attain,
         "cpu_baseline": cpu,
+        "source": source_identity(),
     }
     if graph is not None:
         out["graph"] = graph

@@ -51,11 +51,20 @@ extern "C" {
                                  N outside [1, M-1], iters < 1, tau not finite
                                  or <= 0, Cin % 32 for mask words            */
 #define LCP_E_UNSUPPORTED -2  /* B not in {32, 64, 128}, M not in {4, 8},
-                                 unknown dtype, or a dtype/mode combination
-                                 the library does not implement              */
+                                 iters * B > LCP_MAX_ITERS_B, unknown dtype,
+                                 or a dtype/mode combination the library
+                                 does not implement                          */
 #define LCP_E_WORKSPACE   -3  /* workspace smaller than the size query says,
                                  or not 256-byte aligned                      */
 #define LCP_E_HIP         -4  /* a kernel launch reported a HIP error         */
+
+/* Largest iters * B the Sinkhorn kernels accept: the reverse pass keeps the
+ * 2 * iters * B fp32 row and column offsets of every iteration of one block in
+ * LDS (64 KB at the limit), so B = 128 allows up to 64 iterations, B = 64 up
+ * to 128 and B = 32 up to 256. Larger products return LCP_E_UNSUPPORTED from
+ * lcp_sinkhorn, lcp_sinkhorn_bwd and every step entry point, before any
+ * launch. */
+#define LCP_MAX_ITERS_B 8192
 
 typedef enum lcp_dtype {
   LCP_F32 = 0,   /* IEEE binary32 */
@@ -90,7 +99,8 @@ typedef struct lcp_layer {
 
 /* Hyper-parameters of one step. */
 typedef struct lcp_cfg {
-  int   iters;  /* Sinkhorn iterations L >= 1 (one = row step then column step) */
+  int   iters;  /* Sinkhorn iterations L >= 1 (one = row step then column step),
+                   iters * B <= LCP_MAX_ITERS_B                                 */
   float tau;    /* temperature > 0                                              */
   int   N, M;   /* keep N of every M; M in {4, 8}, 1 <= N < M, B % M == 0       */
   int   harden; /* 0: the step uses the soft P_hat. 1: the forward uses the
@@ -130,7 +140,8 @@ int lcp_version(void);
  * log-domain form of [blog] section 2.2 (subtract the row log-sum-exp, then the
  * column log-sum-exp, each iteration; exp at the end).
  *   logits: [nb][B][B] fp32 in;  P: [nb][B][B] fp32 out (may alias logits).
- *   B in {32, 64, 128}; iters >= 1; tau finite and > 0.
+ *   B in {32, 64, 128}; iters >= 1 and iters * B <= LCP_MAX_ITERS_B (else
+ *   LCP_E_UNSUPPORTED); tau finite and > 0.
  */
 int lcp_sinkhorn(const float* logits, float* P, int nb, int B, int iters,
                  float tau, void* stream);
@@ -138,7 +149,8 @@ int lcp_sinkhorn(const float* logits, float* P, int nb, int B, int iters,
 /* lcp_sinkhorn_bwd - reverse pass of lcp_sinkhorn: given dE/dP (fp32
  * [nb][B][B]) returns dE/dlogits (fp32 [nb][B][B]). The forward iterations are
  * recomputed from the logits; the derivative of each normalisation follows
- * from [PermLLM] Method 1 by the chain rule. dlogits must not alias dP. */
+ * from [PermLLM] Method 1 by the chain rule. dlogits must not alias dP.
+ * Same limits as lcp_sinkhorn (iters * B <= LCP_MAX_ITERS_B). */
 int lcp_sinkhorn_bwd(const float* logits, const float* dP, int nb, int B,
                      int iters, float tau, float* dlogits, void* stream);
 

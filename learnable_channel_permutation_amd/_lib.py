@@ -21,6 +21,8 @@ LCP_E_UNSUPPORTED = -2
 LCP_E_WORKSPACE = -3
 LCP_E_HIP = -4
 
+LCP_MAX_ITERS_B = 8192   # largest iters * B the Sinkhorn kernels accept
+
 LCP_F32 = 0
 LCP_BF16 = 1
 

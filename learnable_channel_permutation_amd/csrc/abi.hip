@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+
 #include "../../include/lcp.h"
 #include "kernels.h"
 
@@ -12,7 +13,7 @@ using namespace lcp;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxIterB = 8192;   // iters * B bound (Sinkhorn offsets kept in LDS)
+constexpr int kMaxIterB = LCP_MAX_ITERS_B;   // iters * B bound (Sinkhorn offsets kept in LDS)
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

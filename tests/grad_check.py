@@ -1,0 +1,36 @@
+"""Gradient parity helpers for the GPU tests: the oracle's backward taken on
+the mask the GPU's forward chose (the mask is held constant in the backward,
+so a flip near a tie would otherwise add noise unrelated to kernel error),
+compared as a whole and block by block."""
+import numpy as np
+
+import oracle
+from tests.gpu_util import rel_fro, say
+
+
+def oracle_backward_on_mask(lay, spec, logits, bits_rowmajor, hard=False, loss="frobenius", mask_ste=False):
+    """Oracle forward (its own P, or its hard P) with the given row-major mask
+    words, then its backward. Returns (forward dict, backward dict)."""
+    mask = oracle.unpack_bits(np.asarray(bits_rowmajor, dtype=np.uint32), lay.cin)
+    fw = oracle.step_forward(lay.W, lay.X, logits, spec.tau, spec.iters, spec.N, spec.M, mask=mask,
+                             hard=hard, loss=loss)
+    bw = oracle.step_backward(fw, lay.X, lay.W, mask_ste=mask_ste)
+    return fw, bw
+
+
+def check_gradient(got, want, tol=1e-2, block_tol=2e-2, what="dlogits"):
+    """Relative Frobenius error of the whole gradient (<= tol) and of every
+    B x B block (<= block_tol). Blocks whose reference norm is below 1e-6 of
+    the largest block's are compared in absolute terms against that scale."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    r = rel_fro(got, want)
+    norms = np.sqrt(np.sum(want * want, axis=(1, 2)))
+    errs = np.sqrt(np.sum((got - want) ** 2, axis=(1, 2)))
+    scale = np.maximum(norms, 1e-6 * norms.max())
+    per = errs / scale
+    worst = int(np.argmax(per))
+    say("%s rel %.3e, worst block %d rel %.3e" % (what, r, worst, per[worst]))
+    assert r < tol, (what, r)
+    assert per[worst] < block_tol, (what, worst, per[worst])
+    return r, float(per[worst])

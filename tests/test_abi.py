@@ -155,6 +155,23 @@ def test_step_argument_validation():
     assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 1 << 20, 1 << 12, 32, 64)) == L.LCP_E_INVAL
     assert bwd(layer=_lay(L, p, p, 0, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL   # bf16 needs Xt
     assert bwd(n=need - 256) == L.LCP_E_WORKSPACE
+    # iters * B above LCP_MAX_ITERS_B (8192): unsupported, nothing enqueued
+    assert L.LCP_MAX_ITERS_B == 8192
+    assert fwd(cfg=L.lcp_cfg(129, 1.0, 2, 4)) == L.LCP_E_UNSUPPORTED          # 129 * 64 > 8192
+    assert bwd(cfg=L.lcp_cfg(129, 1.0, 2, 4)) == L.LCP_E_UNSUPPORTED
+    big = _lay(L, p, p, p, p, L.LCP_BF16, 64, 256, 32, 128)
+    need128 = L.lcp_step_workspace_bytes(64, 256, 32, 128, 65, L.LCP_BF16)
+    assert fwd(layer=big, cfg=L.lcp_cfg(65, 1.0, 4, 8), n=need128) == L.LCP_E_UNSUPPORTED   # 65 * 128
+    assert bwd(layer=big, cfg=L.lcp_cfg(65, 1.0, 4, 8), n=need128) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_sinkhorn(ctypes.c_void_p(p), ctypes.c_void_p(p), 4, 128, 65, 1.0, None) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_sinkhorn_bwd(ctypes.c_void_p(p), ctypes.c_void_p(p + 4096), 4, 32, 257, 1.0,
+                                ctypes.c_void_p(p + 8192), None) == L.LCP_E_UNSUPPORTED
+    m, vv = ctypes.c_void_p(p + 4096), ctypes.c_void_p(p + 8192)
+    ac = L.lcp_adamw_cfg(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    errs = ctypes.c_void_p(p + 16384)
+    assert lib.lcp_train(ctypes.byref(big), ctypes.c_void_p(p), ctypes.byref(L.lcp_cfg(65, 1.0, 4, 8)), ws,
+                         ctypes.c_size_t(need128), m, vv, 3, ctypes.c_float(1.0), ctypes.c_float(0.1),
+                         ctypes.byref(ac), errs, None) == L.LCP_E_UNSUPPORTED
     # objective and straight-through options
     assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 4, 0, 2, 0)) == L.LCP_E_INVAL            # unknown loss
     assert fwd(cfg=L.lcp_cfg(5, 1.0, 2, 4, 0, 0, 2)) == L.LCP_E_INVAL            # mask_ste not 0/1

@@ -51,3 +51,26 @@ def test_every_profiled_role_names_existing_sources():
         for f in files:
             assert os.path.exists(os.path.join(ROOT, "learnable_channel_permutation_amd", "csrc", f)), (kernel, f)
         assert len(bench.kernel_source_hash(kernel)) == 16
+
+
+def test_kernel_work_of_the_bench_layer():
+    """Algorithmic work per launch on the 4096 x 11008 layer: both GEMMs
+    2 Cout Cin T flops, the fused permute and the adjoint read (and write)
+    the weight-sized matrices once plus one mask bit per weight and P."""
+    import lcp_synth
+    spec = lcp_synth.DOWN_PROJ_4096x11008
+    names = ["layer_init", "sinkhorn_fwd", "permute_mask_unpermute", "error_gemm", "dD_gemm", "block_adjoint"]
+    w = bench.kernel_work(spec, names)
+    assert w["error_gemm"] == ("flops", 2.0 * 4096 * 11008 * 2048) == w["dD_gemm"]
+    kind, nbytes = w["block_adjoint"]
+    assert kind == "bytes" and nbytes == 4 * 4096 * 11008 + 4096 * 11008 // 8 + 4 * 172 * 64 * 64
+    kind, nbytes = w["permute_mask_unpermute"]
+    assert kind == "bytes" and nbytes == 4 * 4096 * 11008 + 4096 * 11008 // 8 + 4 * 172 * 64 * 64
+    kind, nbytes = w["layer_init"]
+    assert kind == "bytes" and nbytes == 2 * 2048 * 11008 * 2 + 4 * 11008
+
+
+def test_source_identity_hashes_the_library_sources():
+    ident = bench.source_identity()
+    assert len(ident["csrc_sha16"]) == 16
+    assert ident["git"] is None or len(ident["git"]) == 12
