@@ -20,17 +20,23 @@ def oracle_backward_on_mask(lay, spec, logits, bits_rowmajor, hard=False, loss="
 
 def check_gradient(got, want, tol=1e-2, block_tol=2e-2, what="dlogits"):
     """Relative Frobenius error of the whole gradient (<= tol) and of every
-    B x B block (<= block_tol). Blocks whose reference norm is below 1e-6 of
-    the largest block's are compared in absolute terms against that scale."""
+    B x B block (<= block_tol). A block's error is taken relative to the
+    larger of its own norm and the RMS block norm ||want|| / sqrt(nb): a block
+    whose gradient nearly cancels (its terms large, their sum small) carries
+    the rounding of its terms, not of its sum, while an error confined to a
+    few row tiles of one block still shows against a typical block's norm."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     r = rel_fro(got, want)
     norms = np.sqrt(np.sum(want * want, axis=(1, 2)))
     errs = np.sqrt(np.sum((got - want) ** 2, axis=(1, 2)))
-    scale = np.maximum(norms, 1e-6 * norms.max())
+    scale = np.maximum(norms, np.linalg.norm(want) / np.sqrt(len(norms)))
     per = errs / scale
     worst = int(np.argmax(per))
-    say("%s rel %.3e, worst block %d rel %.3e" % (what, r, worst, per[worst]))
+    order = np.argsort(per)[::-1][:3]
+    say("%s rel %.3e, worst blocks %s (norm / max block norm %s)"
+        % (what, r, ", ".join("%d: %.3e" % (b, per[b]) for b in order),
+           ", ".join("%.3f" % (norms[b] / norms.max()) for b in order)))
     assert r < tol, (what, r)
     assert per[worst] < block_tol, (what, worst, per[worst])
     return r, float(per[worst])
