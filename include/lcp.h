@@ -25,7 +25,8 @@
  *   - Every pointer argument is a device pointer owned by the caller, except
  *     the lcp_layer / lcp_cfg / lcp_timing structs and size_t* outputs, which
  *     live in host memory. The library never allocates, frees or synchronises,
- *     holds no global mutable state and is reentrant. Work is enqueued on the
+ *     holds no global mutable state and is reentrant (the one exception is the
+ *     fixed device scratch of lcp_layer_outputs_noalloc, described there). Work is enqueued on the
  *     given HIP stream (a hipStream_t passed as void*; NULL = null stream) and
  *     runs asynchronously.
  *   - Inputs are never written. Outputs are fully overwritten.
@@ -57,6 +58,8 @@ extern "C" {
 #define LCP_E_WORKSPACE   -3  /* workspace smaller than the size query says,
                                  or not 256-byte aligned                      */
 #define LCP_E_HIP         -4  /* a kernel launch reported a HIP error         */
+#define LCP_E_SCRATCH     -5  /* the input needs more than the fixed scratch
+                                 of an allocation-free entry point            */
 
 /* Largest iters * B the Sinkhorn kernels accept: the reverse pass keeps the
  * 2 * iters * B fp32 row and column offsets of every iteration of one block in
@@ -241,6 +244,28 @@ int lcp_error(const void* W, const void* Wt, const void* X, lcp_dtype dt,
 int lcp_layer_outputs(const void* W, const void* X, lcp_dtype dt, int cout,
                       int cin, int T, void* Y, float* y2, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* lcp_layer_outputs_noalloc - lcp_layer_outputs without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments minus
+ * ws / ws_bytes, same kernels, bit-identical Y and *y2.
+ * The partial sums of ||Y||^2 (one fp32 per GEMM workgroup) live in a fixed
+ * device array inside the library, LCP_NOALLOC_MAX_PARTS floats (64 KB),
+ * which every GPU the library runs on holds until the process ends. The
+ * partial count is ceil(cout / 256) * ceil(pitch / 128) for BF16 and
+ * ceil(cout / ts) * ceil(pitch / ts) for F32 (ts = 64, or 32 when 64-wide
+ * tiles would number fewer than 128), pitch = lcp_xt_pitch(T); a shape that
+ * needs more returns LCP_E_SCRATCH before any launch (a 4096 x 11008 BF16
+ * layer with 2048 tokens needs 256). The first call on a device looks the array's
+ * address up with that device current (the current HIP device must be the
+ * stream's). Nothing is allocated, freed or cleared: each workgroup
+ * overwrites its own partial. All calls on one GPU share the array, so calls
+ * that overlap on one GPU (other streams or threads) race; calls ordered on
+ * one stream do not. */
+#define LCP_NOALLOC_MAX_PARTS 16384
+int lcp_layer_outputs_noalloc(const void* W, const void* X, lcp_dtype dt,
+                              int cout, int cin, int T, void* Y, float* y2,
+                              void* stream);
 
 /* ---------------------------------------------------------------------------
  * Full step. The workspace carries the forward's saved state (P, Sinkhorn

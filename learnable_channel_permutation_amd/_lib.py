@@ -21,7 +21,10 @@ LCP_E_UNSUPPORTED = -2
 LCP_E_WORKSPACE = -3
 LCP_E_HIP = -4
 
+LCP_E_SCRATCH = -5
+
 LCP_MAX_ITERS_B = 8192   # largest iters * B the Sinkhorn kernels accept
+LCP_NOALLOC_MAX_PARTS = 16384   # partial sums held by lcp_layer_outputs_noalloc's fixed scratch
 
 LCP_F32 = 0
 LCP_BF16 = 1
@@ -34,7 +37,7 @@ EXPORTS = [
     "lcp_xt_pitch", "lcp_layer_init", "lcp_permute", "lcp_nm_mask",
     "lcp_error_workspace_bytes", "lcp_error", "lcp_step_workspace_bytes", "lcp_step_fwd",
     "lcp_step_bwd", "lcp_harden", "lcp_adamw", "lcp_step_bwd_adamw", "lcp_train",
-    "lcp_layer_outputs", "lcp_sparse_pack_bytes", "lcp_sparse_pack", "lcp_gather_channels",
+    "lcp_layer_outputs", "lcp_layer_outputs_noalloc", "lcp_sparse_pack_bytes", "lcp_sparse_pack", "lcp_gather_channels",
     "lcp_sparse_gemm", "lcp_deploy_forward",
 ]
 
@@ -93,6 +96,7 @@ def _load():
         "lcp_error_workspace_bytes": (i, [i, i, i, i, psz]),
         "lcp_error": (i, [vp, vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
         "lcp_layer_outputs": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
+        "lcp_layer_outputs_noalloc": (i, [vp, vp, i, i, i, i, vp, vp, vp]),
         "lcp_sparse_pack_bytes": (i, [i, i, psz, psz]),
         "lcp_sparse_pack": (i, [vp, i, i, i, vp, vp, vp, vp, vp]),
         "lcp_gather_channels": (i, [vp, i, i, i, vp, vp, vp]),
@@ -215,6 +219,14 @@ def lcp_layer_outputs(W, X, Y, y2, ws, stream=None):
     return _check("lcp_layer_outputs",
                   LIB.lcp_layer_outputs(_p(W), _p(X), dtype_code(W), cout, cin, T, _p(Y), _p(y2), _p(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lcp_layer_outputs_noalloc(W, X, Y, y2, stream=None):
+    cout, cin = W.shape
+    T = X.shape[0]
+    return _check("lcp_layer_outputs_noalloc",
+                  LIB.lcp_layer_outputs_noalloc(_p(W), _p(X), dtype_code(W), cout, cin, T, _p(Y), _p(y2),
+                                                _stream(stream)))
 
 
 def lcp_step_workspace_bytes(cout, cin, T, B, iters, dtype):

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/lcp.h"
 #include "kernels.h"
@@ -170,6 +171,35 @@ static int step_bwd_impl(const lcp_layer* L, const float* logits, const lcp_cfg*
 }
 
 
+// ---- allocation-free variant of lcp_layer_outputs ----------------------------
+// The error GEMM's per-workgroup partial sums of ||Y||^2 live in this fixed
+// device array instead of a caller workspace. Every GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` is only a
+// host-side stand-in: kernels get the device address looked up once per
+// device with hipGetSymbolAddress (kept in g_scratch_dev) and never the name.
+__device__ __attribute__((aligned(256))) float scratch[LCP_NOALLOC_MAX_PARTS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices];   // device address of `scratch` per device, null until first use
+
+// Address of `scratch` on the current device; looked up with that device
+// current on the first call there.
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LCP_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return LCP_E_HIP;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return LCP_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* lcp_status_string(int code) {
@@ -179,6 +209,7 @@ const char* lcp_status_string(int code) {
     case LCP_E_UNSUPPORTED: return "unsupported configuration";
     case LCP_E_WORKSPACE: return "workspace too small or misaligned";
     case LCP_E_HIP: return "HIP launch error";
+    case LCP_E_SCRATCH: return "input exceeds the fixed scratch of an allocation-free entry point";
   }
   return "unknown status";
 }
@@ -328,6 +359,32 @@ int lcp_layer_outputs(const void* W, const void* X, lcp_dtype dt, int cout, int 
   const int nparts = gemm_error_parts(cout, pitch, dt == LCP_BF16);
   float* part = (float*)ws;
   hipStream_t s = S(stream);
+  if (dt == LCP_BF16)
+    LCP_RUN(launch_gemm_error_bf16((const uint16_t*)W, cin, (const uint16_t*)X, cin, cout, T, pitch, cin,
+                                   (uint16_t*)Y, pitch, part, nullptr, nullptr, s));
+  else
+    LCP_RUN(launch_gemm_error_f32((const float*)W, cin, (const float*)X, cin, cout, T, pitch, cin, (float*)Y,
+                                  pitch, part, nullptr, nullptr, s));
+  LCP_RUN(launch_sum_finalize(part, nparts, y2, s));
+  return LCP_OK;
+}
+
+// Same kernels as lcp_layer_outputs, partial sums in the fixed scratch.
+int lcp_layer_outputs_noalloc(const void* W, const void* X, lcp_dtype dt, int cout, int cin, int T, void* Y,
+                              float* y2, void* stream) {
+  if (!W || !X || !Y || !y2 || cout <= 0 || cin <= 0 || T <= 0) return LCP_E_INVAL;
+  if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
+  if (cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LCP_E_INVAL;
+  const int pitch = pitch_of(T);
+  const int nparts = gemm_error_parts(cout, pitch, dt == LCP_BF16);
+  if (nparts > LCP_NOALLOC_MAX_PARTS) return LCP_E_SCRATCH;
+  float* part = nullptr;
+  const int rc = scratch_on_current_device(&part);
+  if (rc != LCP_OK) return rc;
+  hipStream_t s = S(stream);
+  // the same kernels as lcp_layer_outputs; each workgroup overwrites its own
+  // partial, so nothing needs clearing between calls
   if (dt == LCP_BF16)
     LCP_RUN(launch_gemm_error_bf16((const uint16_t*)W, cin, (const uint16_t*)X, cin, cout, T, pitch, cin,
                                    (uint16_t*)Y, pitch, part, nullptr, nullptr, s));

@@ -190,6 +190,28 @@ def test_step_argument_validation():
     assert lib.lcp_layer_outputs(p, p, L.LCP_BF16, 8, 64, 16, p, p, p, ctypes.c_size_t(16), s) == L.LCP_E_WORKSPACE
 
 
+def test_noalloc_argument_validation():
+    """lcp_layer_outputs_noalloc rejects bad arguments and shapes whose
+    partial sums exceed its fixed scratch before any HIP call (this runs on a
+    machine without a GPU)."""
+    L = _lib()
+    lib = L.LIB
+    p = ctypes.c_void_p(0x100000)
+    s = None
+    assert L.LCP_NOALLOC_MAX_PARTS == 16384
+    assert L.status_string(L.LCP_E_SCRATCH) not in ("ok", "unknown status")
+    assert lib.lcp_layer_outputs_noalloc(None, p, L.LCP_BF16, 8, 64, 16, p, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_layer_outputs_noalloc(p, p, L.LCP_BF16, 8, 64, 16, None, p, s) == L.LCP_E_INVAL
+    assert lib.lcp_layer_outputs_noalloc(p, p, L.LCP_BF16, 8, 48, 16, p, p, s) == L.LCP_E_INVAL     # cin % 32
+    assert lib.lcp_layer_outputs_noalloc(p, p, 9, 8, 64, 16, p, p, s) == L.LCP_E_UNSUPPORTED
+    assert lib.lcp_layer_outputs_noalloc(ctypes.c_void_p(0x100008), p, L.LCP_BF16, 8, 64, 16, p, p,
+                                         s) == L.LCP_E_INVAL                                      # alignment
+    # bf16: ceil(cout / 256) * ceil(pitch / 128) partials; 128 * 129 > 16384
+    assert lib.lcp_layer_outputs_noalloc(p, p, L.LCP_BF16, 128 * 256, 32, 129 * 128, p, p, s) == L.LCP_E_SCRATCH
+    # f32: 64-wide tiles, 129 * 128 > 16384
+    assert lib.lcp_layer_outputs_noalloc(p, p, L.LCP_F32, 129 * 64, 32, 128 * 64, p, p, s) == L.LCP_E_SCRATCH
+
+
 def test_deploy_argument_validation():
     """Deploy entry points reject bad sizes, block sizes and alignment before
     any launch (no GPU needed: nothing is enqueued on an error)."""
