@@ -12,6 +12,11 @@ Inputs are resident in HBM before the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--breakdown]
 
+Warm-up runs at least W steps and at least --warmup-seconds (1 s) of steps
+(`warmup_run` records both): on MI355X the clocks take longer than a few steps
+to settle, and 5 warm-up steps leave the 20 timed ones about 7 % slower than
+the steady state a training loop on one layer runs at.
+
 Prints one JSON line. `value` is steps/s from the median step time (an event
 at every step boundary of the K timed steps; `ms_per_step` is their mean).
 `roofline` is computed from the average duration of the dominant kernel,
@@ -49,6 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep warming up (whole steps) until at least this much time has passed as well as "
+                         "--warmup steps: the GPU's clocks take longer than a few steps to settle")
     ap.add_argument("--config", type=int, default=None, help="layer config index (default: the bench layer)")
     ap.add_argument("--breakdown", action="store_true", help="also print the per-kernel times to stderr")
     ap.add_argument("--no-kernels", action="store_true",
@@ -498,9 +506,17 @@ def main():
         elif spec.backward:
             sess.backward(logits, dlogits, timing=tb)
 
-    for _ in range(args.warmup):
+    # untimed warm-up: at least --warmup steps and at least --warmup-seconds
+    # of stepping (synchronised every 8 steps so wall time follows the GPU)
+    t_w0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w0 < args.warmup_seconds:
         step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_info = {"steps": n_warm, "seconds": round(time.perf_counter() - t_w0, 3)}
 
     # timed region: whole steps, plus events around the two GEMMs on the same stream
     K = args.steps
@@ -632,6 +648,7 @@ def main():
         "ms_per_step_median": round(ms_median, 4),
         "value_from": "median step time (event at every step boundary); ms_per_step is the mean over the K steps",
         "value_mean": round(1000.0 / ms, 2),
+        "warmup_run": warm_info,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
