@@ -450,6 +450,28 @@ def saturating_kernels(lcp, torch, he):
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"us": round(ms * 1e3, 1), "GB_per_s": round(gbs, 1), "frac_of_8TBs": round(gbs / 8000.0, 3),
                      "bytes": nbytes}
+    # the same traffic as a plain device copy (torch's copy kernel): the
+    # Sinkhorn reads and writes nb B^2 floats, the mask reads the scores
+    for name, nin, nout in (("sinkhorn_fwd_17792x64x64", nb * B * B, nb * B * B),
+                            ("nm_mask_28672x8192", rows * cin, rows * cin // 32)):
+        a = torch.ones(nin, dtype=torch.float32, device=dev)
+        c = torch.empty(nout, dtype=torch.float32, device=dev)
+        fn = (lambda: c.copy_(a)) if nin == nout else (lambda: torch.sum(a))
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
+        cgbs = (4 * nin + (4 * nout if nin == nout else 0)) / (cms * 1e-3) / 1e9
+        out[name]["reference"] = {"kind": "device copy" if nin == nout else "torch.sum read", "us": round(cms * 1e3, 1),
+                                  "GB_per_s": round(cgbs, 1)}
+        out[name]["frac_of_reference"] = round(out[name]["GB_per_s"] / cgbs, 3)
+        del a, c
     return out
 
 

@@ -11,13 +11,18 @@
 // (a < 4) and columns lc*CPL + c (c < CPL = B/16), all in registers for every
 // iteration (no HBM or LDS round trip of the block). Row reductions run over
 // the 16 lanes of a DPP row; column reductions pair lanes 16 and 32 apart
-// (permlane swaps), then the waves' (max, sum) pairs meet in LDS: wave w
-// merges the pairs of columns 16w .. 16w+15 (four lanes per column, each
-// taking every fourth wave, merged across lanes 16 and 32 apart) and
-// publishes the column offsets, two barriers per column step. Work is done in base 2:
-// z = logits * log2(e) / tau, lse2 = max + log2(sum exp2(z - max)), so each
-// normalisation costs one v_exp_f32 per element. The row offsets r_i and
-// column offsets c_i (base 2) are kept for the reverse pass.
+// (permlane swaps), then the waves' partial sums meet in LDS: wave w merges
+// columns 16w .. 16w+15 (four lanes per column, each taking every fourth
+// wave, merged across lanes 16 and 32 apart) and publishes the column
+// results, two barriers per column step. Work is done in base 2:
+// z = logits * log2(e) / tau.
+// The forward exponentiates the block once (K = exp2(z - row max)) and
+// iterates row and column scalings on it, one multiply-add per element and
+// normalisation (the iterates are diag(u) K diag(v) exactly as the
+// log-domain ones are exp2 of Z^i); a block whose row or column sum leaves
+// the range where that is accurate restarts on the exact log-domain
+// iteration. The row offsets r_i and column offsets c_i (base 2) of every
+// iteration are kept for the reverse pass, which works in the log domain.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,13 +35,15 @@ struct SkGeom {
   static constexpr int CPL = B / 16;
 };
 
-// CPL consecutive floats (16-byte aligned for CPL >= 4, 8-byte for CPL = 2)
-template <int CPL>
+// CPL consecutive floats (16-byte aligned for CPL >= 4, 8-byte for CPL = 2);
+// NT: non-temporal access (data used once, kept out of the caches)
+template <int CPL, bool NT = false>
 __device__ __forceinline__ void ld_cols(const float* p, float (&v)[CPL]) {
   if constexpr (CPL % 4 == 0) {
 #pragma unroll
     for (int c = 0; c < CPL; c += 4) {
-      const floatx4 q = *reinterpret_cast<const floatx4*>(p + c);
+      const floatx4* a = reinterpret_cast<const floatx4*>(p + c);
+      const floatx4 q = NT ? __builtin_nontemporal_load(a) : *a;
       v[c] = q[0]; v[c + 1] = q[1]; v[c + 2] = q[2]; v[c + 3] = q[3];
     }
   } else {
@@ -47,11 +54,16 @@ __device__ __forceinline__ void ld_cols(const float* p, float (&v)[CPL]) {
     }
   }
 }
-template <int CPL>
+template <int CPL, bool NT = false>
 __device__ __forceinline__ void st_cols(float* p, const float (&v)[CPL]) {
   if constexpr (CPL % 4 == 0) {
 #pragma unroll
-    for (int c = 0; c < CPL; c += 4) *reinterpret_cast<floatx4*>(p + c) = floatx4{v[c], v[c + 1], v[c + 2], v[c + 3]};
+    for (int c = 0; c < CPL; c += 4) {
+      const floatx4 q = floatx4{v[c], v[c + 1], v[c + 2], v[c + 3]};
+      floatx4* a = reinterpret_cast<floatx4*>(p + c);
+      if (NT) __builtin_nontemporal_store(q, a);
+      else *a = q;
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < CPL; c += 2) *reinterpret_cast<float2*>(p + c) = float2{v[c], v[c + 1]};
@@ -59,12 +71,12 @@ __device__ __forceinline__ void st_cols(float* p, const float (&v)[CPL]) {
 }
 
 // The lane's 4 x CPL elements of a row-major B x B block.
-template <int B>
+template <int B, bool NT = false>
 __device__ __forceinline__ void ld_block(const float* __restrict__ src, float (&v)[4][SkGeom<B>::CPL], int w,
                                          int lr, int lc) {
   constexpr int CPL = SkGeom<B>::CPL;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) ld_cols<CPL>(src + (16 * w + 4 * lr + a) * B + lc * CPL, v[a]);
+  for (int a = 0; a < 4; ++a) ld_cols<CPL, NT>(src + (16 * w + 4 * lr + a) * B + lc * CPL, v[a]);
 }
 
 // Value of the lane 16 (or 32) apart, from the permlane swaps (the swap
@@ -191,11 +203,34 @@ __device__ __forceinline__ void sk_iter(float (&z)[4][SkGeom<B>::CPL], float2* r
   }
 }
 
+// Quad broadcast (DPP quad_perm [a, a, a, a]): every lane of a quad gets the
+// value of the quad's lane a.
+template <int A>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return dpp<A | (A << 2) | (A << 4) | (A << 6)>(v);
+}
+
+// Smallest row or column sum the scaled iteration accepts. Scalings stay
+// below 2^45 each, so an entry whose exponential underflowed (K < 2^-126)
+// stands for P < 2^-36: below the parity tolerance's absolute floor, and a
+// negligible share (< 2^-36) of every sum it belongs to.
+constexpr float kScaledFloor = 0x1p-45f;
+
 // Forward: P = exp2(Z^L); optional offsets off[b][i][0][row], off[b][i][1][col].
+// The iterations run on scalings of a block exponentiated once
+// (Sinkhorn-Knopp in the form of Schmitzer's stabilized scaling): with
+// K_jk = exp2(z_jk - m_j), m_j the row maximum, every iterate is
+// exp2(Z^i) = diag(u) K diag(v), so one row step is u_j = 1 / sum_k K_jk v_k
+// and one column step v_k = 1 / sum_j K_jk u_j: one multiply-add per element
+// and step, no exponential. The log-domain offsets of iteration i follow from
+// the sums (row: r = log2 s_i - log2 s_(i-1), with m_j + log2 s_1 for i = 1;
+// column alike with t), so the reverse pass rebuilds Z^i from them as from the
+// log-domain forward. If any sum falls below kScaledFloor the block restarts
+// on the log-domain iteration of sk_iter (block-uniform decision).
 // With fwd != nullptr the block of P and its column norms are staged in LDS
 // and the MFMA operand fragments (frag.h) are written as well.
-template <int B>
-__global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
+template <int B, bool OFFS, bool FRAGS>
+__global__ __launch_bounds__(SkGeom<B>::THREADS) __attribute__((amdgpu_waves_per_eu(B == 128 ? 4 : 8))) void sinkhorn_fwd_kernel(
     const float* __restrict__ logits, float* P, float* __restrict__ off, int iters, float scale,
     const float* __restrict__ n, u32x4* __restrict__ fwd, u32x4* __restrict__ adj) {
   constexpr int CPL = SkGeom<B>::CPL;
@@ -203,35 +238,136 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_fwd_kernel(
   constexpr int PP = B + 2;                       // LDS row pitch of the staged block
   __shared__ float2 red[2][WAVES * B];
   __shared__ __attribute__((aligned(16))) float ccb[B];
+  __shared__ __attribute__((aligned(16))) float vsh[2][B];
   __shared__ int skflag[2];
   extern __shared__ float ps[];                   // [B][PP] P block, then [B] norms
   const int b = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l >> 4, lc = l & 15;
-  float z[4][CPL];
-  ld_block<B>(logits + (size_t)b * B * B, z, w, lr, lc);
+  const int q = lc & 3;                           // the row 4 lr + q of this lane's quad position
+  const float* src = logits + (size_t)b * B * B;
+  float* ob = OFFS ? off + (size_t)b * iters * 2 * B : nullptr;
+
+  // the standalone call (no offsets) reads each logit once and writes each
+  // entry of P once: non-temporal; the step's logits and P are read again
+  constexpr bool NT = !OFFS;
+  float K[4][CPL];                                 // exp2(z - m), at the end the block of P
+  ld_block<B, NT>(src, K, w, lr, lc);
+  float m[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 4; ++a) {
+    float mm = -__builtin_inff();
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) z[a][c] *= scale;
-  for (int it = 0; it < iters; ++it) {
-    float* ro = off ? off + ((size_t)(b * iters + it) * 2 + 0) * B : nullptr;
-    float* co = off ? off + ((size_t)(b * iters + it) * 2 + 1) * B : nullptr;
-    sk_iter<B>(z, red[it & 1], ccb, &skflag[it & 1], ro, co, w, lr, lc);
+    for (int c = 0; c < CPL; ++c) {
+      K[a][c] *= scale;
+      mm = fmaxf(mm, K[a][c]);
+    }
+    m[a] = row16_max(mm);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) K[a][c] = exp2_(K[a][c] - m[a]);
   }
+  const float m_mine = q == 0 ? m[0] : q == 1 ? m[1] : q == 2 ? m[2] : m[3];
+
+  float v[CPL], u[4];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) v[c] = 1.f;
+  float ls_prev = 0.f, lt_prev = 0.f;             // log2 of this lane's previous row / column sum
+  bool scaled = true;
+  for (int it = 0; it < iters; ++it) {
+    float* rg = reinterpret_cast<float*>(red[it & 1]);
+    if (w == 0 && l == 0) skflag[it & 1] = 0;
+    // ---- row step: s_j = sum_k K_jk v_k, u_j = 1 / s_j (lane q of each
+    // quad takes row 4 lr + q, the quad shares the four results)
+    float s[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float acc = K[a][0] * v[0];
+#pragma unroll
+      for (int c = 1; c < CPL; ++c) acc = fmaf(K[a][c], v[c], acc);
+      s[a] = row16_sum(acc);
+    }
+    const float s_mine = q == 0 ? s[0] : q == 1 ? s[1] : q == 2 ? s[2] : s[3];
+    const bool row_bad = !(s_mine >= kScaledFloor);
+    const float u_mine = __builtin_amdgcn_rcpf(s_mine);
+    u[0] = quad_bcast<0>(u_mine);
+    u[1] = quad_bcast<1>(u_mine);
+    u[2] = quad_bcast<2>(u_mine);
+    u[3] = quad_bcast<3>(u_mine);
+    if (OFFS) {
+      const float ls = log2_(s_mine);
+      if (lc < 4) ob[(2 * it) * B + 16 * w + 4 * lr + q] = (it == 0) ? m_mine + ls : ls - ls_prev;
+      ls_prev = ls;
+    }
+    // ---- column step: t_k = sum_j K_jk u_j over the lane's rows, the wave's
+    // 16 rows (lanes 16 and 32 apart), then the waves (LDS)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float acc = K[0][c] * u[0];
+#pragma unroll
+      for (int a = 1; a < 4; ++a) acc = fmaf(K[a][c], u[a], acc);
+      acc = xor32_sum(xor16_sum(acc));
+      if (lr == 0) rg[w * B + lc * CPL + c] = acc;
+    }
+    __syncthreads();
+    {
+      const int col = 16 * w + lc;
+      float tk = 0.f;
+#pragma unroll
+      for (int vw = lr; vw < WAVES; vw += 4) tk += rg[vw * B + col];
+      tk += partner16(tk, l);
+      tk += partner32(tk, l);
+      if (row_bad || !(tk >= kScaledFloor)) skflag[it & 1] = 1;
+      if (lr == 0) vsh[it & 1][col] = __builtin_amdgcn_rcpf(tk);
+      if (OFFS) {
+        const float lt = log2_(tk);
+        if (lr == 0) ob[(2 * it + 1) * B + col] = (it == 0) ? lt : lt - lt_prev;
+        lt_prev = lt;
+      }
+    }
+    __syncthreads();
+    if (skflag[it & 1] != 0) {                    // block-uniform
+      scaled = false;
+      break;
+    }
+    ld_cols<CPL>(&vsh[it & 1][lc * CPL], v);
+  }
+
+  if (scaled) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) K[a][c] = (K[a][c] * u[a]) * v[c];
+  } else {
+    // exact log-domain restart of the whole block (every thread has read the
+    // flag before sk_iter reuses it)
+    __syncthreads();
+    float z[4][CPL];
+    ld_block<B>(src, z, w, lr, lc);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) z[a][c] *= scale;
+    for (int it = 0; it < iters; ++it) {
+      float* ro = OFFS ? ob + (2 * it) * B : nullptr;
+      float* co = OFFS ? ob + (2 * it + 1) * B : nullptr;
+      sk_iter<B>(z, red[it & 1], ccb, &skflag[it & 1], ro, co, w, lr, lc);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) K[a][c] = exp2_(z[a][c]);
+  }
+
   float* dst = P + (size_t)b * B * B;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int row = 16 * w + 4 * lr + a;
-    float v[CPL];
+    st_cols<CPL, NT>(dst + row * B + lc * CPL, K[a]);
+    if (FRAGS) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = exp2_(z[a][c]);
-    st_cols<CPL>(dst + row * B + lc * CPL, v);
-    if (fwd != nullptr) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) ps[row * PP + lc * CPL + c] = v[c];
+      for (int c = 0; c < CPL; ++c) ps[row * PP + lc * CPL + c] = K[a][c];
     }
   }
-  if (fwd != nullptr) {
+  if (FRAGS) {
     for (int i = t; i < B; i += SkGeom<B>::THREADS) ps[B * PP + i] = n[(size_t)b * B + i];
     __syncthreads();
     frag_build<B, PP>(ps, ps + B * PP, fwd + (size_t)b * FragGeom<B>::NARR * FragGeom<B>::FRAG,
@@ -450,10 +586,14 @@ hipError_t launch_sinkhorn_fwd(const float* logits, float* P, float* off, int nb
                                hipStream_t s) {
   const float scale = sk_scale(tau);
   const size_t lds = fwd ? (size_t)(B * (B + 2) + B) * sizeof(float) : 0;
+  // variants: plain (no offsets, no fragments), offsets only (fp32 layers),
+  // offsets and fragments (bf16 layers)
+  const bool o = off != nullptr, f = fwd != nullptr;
+  if (f && !o) return hipErrorInvalidValue;
   switch (B) {
-    case 32: sinkhorn_fwd_kernel<32><<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
-    case 64: sinkhorn_fwd_kernel<64><<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
-    case 128: sinkhorn_fwd_kernel<128><<<nb, SkGeom<128>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
+    case 32: (f ? sinkhorn_fwd_kernel<32, true, true> : o ? sinkhorn_fwd_kernel<32, true, false> : sinkhorn_fwd_kernel<32, false, false>)<<<nb, SkGeom<32>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
+    case 64: (f ? sinkhorn_fwd_kernel<64, true, true> : o ? sinkhorn_fwd_kernel<64, true, false> : sinkhorn_fwd_kernel<64, false, false>)<<<nb, SkGeom<64>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
+    case 128: (f ? sinkhorn_fwd_kernel<128, true, true> : o ? sinkhorn_fwd_kernel<128, true, false> : sinkhorn_fwd_kernel<128, false, false>)<<<nb, SkGeom<128>::THREADS, lds, s>>>(logits, P, off, iters, scale, n, fwd, adj); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
