@@ -34,7 +34,9 @@
  *     nothing was enqueued and nothing written. Results are deterministic
  *     (no atomics in reductions): equal inputs give bitwise-equal outputs.
  *   - Sizes are limited to what 32-bit element indices of one matrix hold
- *     (rows * cols < 2^31).
+ *     (rows * cols < 2^31); for BF16 layers W and X (and every bf16 matrix a
+ *     GEMM reads) must also stay below 2^30 elements (2 GB), else
+ *     LCP_E_INVAL.
  */
 #ifndef LCP_H
 #define LCP_H

@@ -22,6 +22,10 @@ inline bool good_dtype(lcp_dtype d) { return d == LCP_F32 || d == LCP_BF16; }
 inline size_t esize(lcp_dtype d) { return d == LCP_BF16 ? 2 : 4; }
 inline bool good_B(int B) { return B == 32 || B == 64 || B == 128; }
 inline bool fits_i32(long long a, long long b) { return a > 0 && b > 0 && a * b < (1LL << 31); }
+// bf16 GEMM operands are read through buffer resources whose zero reads
+// (K tail, rows past the matrix) use an offset of 2^31 bytes: every bf16
+// matrix a GEMM reads must stay below 2^30 elements (2 GB)
+inline bool fits_bf16_gemm(long long a, long long b) { return a > 0 && b > 0 && a * b < (1LL << 30); }
 inline bool good_tau(float tau) { return isfinite(tau) && tau > 0.f; }
 inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int pitch_of(int T) { return (T + 63) / 64 * 64; }
@@ -75,6 +79,7 @@ int check_step_args(const lcp_layer* L, const float* logits, const lcp_cfg* c) {
   if (!fits_i32(L->cout, L->cin) || !fits_i32(L->T, L->cin) || !fits_i32(L->cout, pitch_of(L->T)) ||
       !fits_i32(L->cin, pitch_of(L->T)))
     return LCP_E_INVAL;
+  if (L->dtype == LCP_BF16 && (!fits_bf16_gemm(L->cout, L->cin) || !fits_bf16_gemm(L->T, L->cin))) return LCP_E_INVAL;
   if (!aligned16(L->W) || !aligned16(L->X) || !aligned16(logits)) return LCP_E_INVAL;
   return LCP_OK;
 }
@@ -318,6 +323,7 @@ int lcp_error(const void* W, const void* Wt, const void* X, lcp_dtype dt, int co
   if (!W || !Wt || !X || !err || cout <= 0 || cin <= 0 || T <= 0) return LCP_E_INVAL;
   if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
   if (cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  if (dt == LCP_BF16 && (!fits_bf16_gemm(cout, cin) || !fits_bf16_gemm(T, cin))) return LCP_E_INVAL;
   if (!aligned16(W) || !aligned16(Wt) || !aligned16(X) || (R_out && !aligned16(R_out))) return LCP_E_INVAL;
   size_t need = 0;
   int rc = lcp_error_workspace_bytes(cout, cin, T, dt, &need);
@@ -349,6 +355,7 @@ int lcp_layer_outputs(const void* W, const void* X, lcp_dtype dt, int cout, int 
   if (!W || !X || !Y || !y2 || cout <= 0 || cin <= 0 || T <= 0) return LCP_E_INVAL;
   if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
   if (cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  if (dt == LCP_BF16 && (!fits_bf16_gemm(cout, cin) || !fits_bf16_gemm(T, cin))) return LCP_E_INVAL;
   if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LCP_E_INVAL;
   size_t need = 0;
   int rc = lcp_error_workspace_bytes(cout, cin, T, dt, &need);
@@ -375,6 +382,7 @@ int lcp_layer_outputs_noalloc(const void* W, const void* X, lcp_dtype dt, int co
   if (!W || !X || !Y || !y2 || cout <= 0 || cin <= 0 || T <= 0) return LCP_E_INVAL;
   if (!good_dtype(dt)) return LCP_E_UNSUPPORTED;
   if (cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(cout, pitch_of(T))) return LCP_E_INVAL;
+  if (dt == LCP_BF16 && (!fits_bf16_gemm(cout, cin) || !fits_bf16_gemm(T, cin))) return LCP_E_INVAL;
   if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LCP_E_INVAL;
   const int pitch = pitch_of(T);
   const int nparts = gemm_error_parts(cout, pitch, dt == LCP_BF16);

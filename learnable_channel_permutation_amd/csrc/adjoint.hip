@@ -124,9 +124,16 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
     // P fragments (MFMA B operand, K = source channel j, N = position k):
     // F[(t*KS + p)*64 + lane][e] = P_b[16p + 8h + e][32t + n]
     if (gfrag != nullptr) {
+      // global -> LDS directly, all of a thread's copies in flight at once
+      // (FRAG is a multiple of 64: each wave copies whole 1 KB rows or none)
       const u32x4* src = gfrag + (size_t)b * Gm::FRAG;
-      u32x4* dst = reinterpret_cast<u32x4*>(fb);
-      for (int e = t; e < Gm::FRAG; e += 256) dst[e] = src[e];
+      constexpr int PER = (Gm::FRAG + 255) / 256;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int e0 = k * 256 + 64 * w;
+        if (e0 < Gm::FRAG) __builtin_amdgcn_global_load_lds(src + e0 + l, (adj_lds_t)(fb + (size_t)e0 * 8), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));   // vmcnt(0)
     } else {
       const float* src = P + (size_t)b * B * B;
       for (int e_idx = t; e_idx < B * B; e_idx += 256) {

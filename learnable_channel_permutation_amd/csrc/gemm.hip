@@ -14,9 +14,11 @@
 // consecutive output columns of one output row. Workgroups are ordered so
 // that each XCD (workgroup id mod 8) works on a compact group of 4 row panels
 // x N column panels, which keeps the panels shared inside that XCD's L2.
-// Out-of-range rows are read from a clamped row (their outputs are never
-// stored); out-of-range K chunks and B rows read a 16-byte zero block, so
-// padded output columns come out exactly zero.
+// Operands are loaded through buffer resources with per-lane offsets fixed
+// per tile (a K step moves only the scalar offset). Out-of-range A rows are
+// read from a clamped row (their outputs are never stored); out-of-range K
+// chunks and B rows of the error product read zeros (offsets past the
+// resource), so padded output columns come out exactly zero.
 //  * gemm_dd_kernel (the backward product): a two-stage ring on 32x32x16
 //    MFMAs, one barrier per K step after which the next tile's loads go out
 //    one at a time between the MFMAs of the first sub-steps; each 16-wide
@@ -43,7 +45,21 @@ constexpr int GROUP_M = 4;
 constexpr int GWM = 4, GWN = 2, GNW = GWM * GWN, GNT = 64 * GNW;   // wave layout, threads
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-__device__ const u32x4 g_zero16[1] = {{0u, 0u, 0u, 0u}};
+
+// Operand loads go through buffer resources: the per-lane byte offset of each
+// load is computed once per tile, and a K step only changes the scalar
+// offset, so issuing a load costs no vector instruction. An offset at or past
+// the resource's size reads zeros (used for rows past the matrix and the K
+// tail). Word 3: 32-bit data format, the only format field raw loads need.
+constexpr uint32_t kOOB = 0x80000000u;                     // an offset past every operand
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const uint16_t* p, size_t elems) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, (int)(uint32_t)(elems * 2),
+                                           0x00020000);
+}
+// 16 bytes at byte offset voff + soff of r into LDS at ldst + 16 * lane
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* ldst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)ldst, 16, (int)voff, (int)soff, 0, 0);
+}
 
 __device__ __forceinline__ void tile_coords(int g, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
   int logical = g;
@@ -87,22 +103,27 @@ __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
   const int h = l >> 5, ln = l & 31;
 
   // load q (< AI: A rows, else B rows) of wave w fills the 64 consecutive
-  // 16-byte chunks (q' * GNW + w) * 64 + lane of its matrix in the stage
+  // 16-byte chunks (q' * GNW + w) * 64 + lane of its matrix in the stage.
+  // K is a multiple of GBK here (the transposed activations and the residual
+  // are padded to 64 tokens), so no K tail; rows past M or N_valid read a
+  // clamped row (those outputs are never stored). Each load's byte offset
+  // from the matrix origin is computed once; a K step only moves the uniform
+  // base, so the load takes the scalar-base + 32-bit-offset address form.
   constexpr int NL = AI + BI;                              // load instructions per tile
+  const __amdgpu_buffer_rsrc_t rA = operand_rsrc(A, (size_t)M * lda), rB = operand_rsrc(Bm, (size_t)N_valid * ldb);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t voff[NL];
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int qq = q < AI ? q : q - AI;
+    const int c = (qq * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+    if (q < AI) voff[q] = (uint32_t)(((size_t)min(m0 + row, M - 1) * lda + ch * 8) * 2);
+    else voff[q] = (uint32_t)(((size_t)min(n0 + row, N_valid - 1) * ldb + ch * 8) * 2);
+  }
   auto issue_one = [&](int stage, int k0, int q) {
-    uint16_t* sb = lds + stage * STAGE;
-    if (q < AI) {
-      const int c = (q * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
-      const int gm = min(m0 + row, M - 1), gk = k0 + ch * 8;
-      const void* src = (gk < K) ? (const void*)(A + (size_t)gm * lda + gk) : (const void*)g_zero16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + (q * GNW + w) * 64 * 8), 16, 0, 0);
-    } else {
-      const int qb = q - AI;
-      const int c = (qb * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
-      const int gn = n0 + row, gk = k0 + ch * 8;
-      const void* src = (gk < K && gn < N_valid) ? (const void*)(Bm + (size_t)gn * ldb + gk) : (const void*)g_zero16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + BM * GBK + (qb * GNW + w) * 64 * 8), 16, 0, 0);
-    }
+    const int qq = q < AI ? q : q - AI;
+    uint16_t* dst = lds + stage * STAGE + (q < AI ? 0 : BM * GBK) + (qq * GNW + wu) * 64 * 8;
+    load16_lds(q < AI ? rA : rB, dst, voff[q], (uint32_t)k0 * 2);
   };
 
   floatx16 acc[FM][FN];
@@ -233,21 +254,29 @@ __global__ __launch_bounds__(GNT, 1) void gemm_err_kernel(
   const int kq = MF == 32 ? (l >> 5) : (l >> 4);
   const int lr = MF == 32 ? (l & 31) : (l & 15);
 
-  // load q of this thread for the tile at k0 into stage `stage`
-  auto issue_one = [&](int stage, int k0, int q) {
-    uint16_t* sb = lds + stage * STAGE;
-    if (q < AI) {
-      const int c = (q * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
-      const int gm = min(m0 + row, M - 1), gk = k0 + ch * 8;
-      const void* src = (gk < K) ? (const void*)(A + (size_t)gm * lda + gk) : (const void*)g_zero16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + (q * GNW + w) * 64 * 8), 16, 0, 0);
-    } else {
-      const int qb = q - AI;
-      const int c = (qb * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
-      const int gn = n0 + row, gk = k0 + ch * 8;
-      const void* src = (gk < K && gn < N_valid) ? (const void*)(Bm + (size_t)gn * ldb + gk) : (const void*)g_zero16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + BM * GBK + (qb * GNW + w) * 64 * 8), 16, 0, 0);
-    }
+  // load q of this thread for the tile at k0 into stage `stage`. Rows past M
+  // read a clamped row (never stored); B rows past N_valid read zeros, so the
+  // padded output columns are exactly zero. In a step whose K chunks reach
+  // past K (the last one when K % 64 != 0) those chunks read zeros too.
+  const __amdgpu_buffer_rsrc_t rA = operand_rsrc(A, (size_t)M * lda), rB = operand_rsrc(Bm, (size_t)N_valid * ldb);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t voff[NL];
+  int kch[NL];                                             // K element offset of each load's chunk
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int qq = q < AI ? q : q - AI;
+    const int c = (qq * GNW + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+    kch[q] = ch * 8;
+    if (q < AI) voff[q] = (uint32_t)(((size_t)min(m0 + row, M - 1) * lda + ch * 8) * 2);
+    else voff[q] = (n0 + row < N_valid) ? (uint32_t)(((size_t)(n0 + row) * ldb + ch * 8) * 2) : kOOB;
+  }
+  // TAIL: the tile at k0 may be the last one (the main loop never loads it)
+  auto issue_one = [&](int stage, int k0, int q, auto TAIL) {
+    const int qq = q < AI ? q : q - AI;
+    uint16_t* dst = lds + stage * STAGE + (q < AI ? 0 : BM * GBK) + (qq * GNW + wu) * 64 * 8;
+    uint32_t vo = voff[q];
+    if (decltype(TAIL)::value && k0 + GBK > K) vo = (k0 + kch[q] < K) ? vo : kOOB;
+    load16_lds(q < AI ? rA : rB, dst, vo, (uint32_t)k0 * 2);
   };
 
   typedef typename std::conditional<MF == 32, floatx16, floatx4>::type acc_t;
@@ -281,7 +310,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_err_kernel(
   // between the MFMAs of sub-steps 0 .. P-2; with NEXT the first fragments of
   // stage `nstage` are read after the barrier. WAIT1: one tile's loads (the
   // ones just issued) may stay in flight at the barrier.
-  auto step = [&](int stage, int lstage, int k0, int nstage, auto LOAD, auto NEXT, auto WAIT1) {
+  auto step = [&](int stage, int lstage, int k0, int nstage, auto LOAD, auto NEXT, auto WAIT1, auto TAIL) {
     constexpr bool DL = decltype(LOAD)::value, DN = decltype(NEXT)::value;
     constexpr int SLOTS = (P - 1) * NM;
 #pragma unroll
@@ -294,7 +323,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_err_kernel(
         for (int o = 0; o < (DL ? NL : 0); ++o)
           if (o * SLOTS / NL == p * NM + m) {
             __builtin_amdgcn_sched_barrier(0);
-            issue_one(lstage, k0, o);
+            issue_one(lstage, k0, o, TAIL);
             __builtin_amdgcn_sched_barrier(0);
           }
         mma(p & 1, m);
@@ -317,32 +346,32 @@ __global__ __launch_bounds__(GNT, 1) void gemm_err_kernel(
   const int nk = (K + GBK - 1) / GBK;
   // tiles 0 and 1 (a tile past K reads zeros and is never multiplied)
 #pragma unroll
-  for (int q = 0; q < NL; ++q) issue_one(0, 0, q);
+  for (int q = 0; q < NL; ++q) issue_one(0, 0, q, Y_{});
 #pragma unroll
-  for (int q = 0; q < NL; ++q) issue_one(1, GBK, q);
+  for (int q = 0; q < NL; ++q) issue_one(1, GBK, q, Y_{});
   wait_vmcnt<NL>();
   __builtin_amdgcn_s_barrier();
   rd(0, 0, 0);
   int kt = 0;
-  for (; kt + 5 < nk; kt += 3) {
-    step(0, 2, (kt + 2) * GBK, 1, Y_{}, Y_{}, Y_{});
-    step(1, 0, (kt + 3) * GBK, 2, Y_{}, Y_{}, Y_{});
-    step(2, 1, (kt + 4) * GBK, 0, Y_{}, Y_{}, Y_{});
+  for (; kt + 5 < nk; kt += 3) {                           // loads tiles kt + 2 .. kt + 4 < nk - 1
+    step(0, 2, (kt + 2) * GBK, 1, Y_{}, Y_{}, Y_{}, N_{});
+    step(1, 0, (kt + 3) * GBK, 2, Y_{}, Y_{}, Y_{}, N_{});
+    step(2, 1, (kt + 4) * GBK, 0, Y_{}, Y_{}, Y_{}, N_{});
   }
   for (; kt < nk; ++kt) {                                  // the last 1 .. 5 tiles
     const int st = kt % RS;
     if (kt + 2 < nk) {
-      if (st == 0) step(0, 2, (kt + 2) * GBK, 1, Y_{}, Y_{}, Y_{});
-      else if (st == 1) step(1, 0, (kt + 2) * GBK, 2, Y_{}, Y_{}, Y_{});
-      else step(2, 1, (kt + 2) * GBK, 0, Y_{}, Y_{}, Y_{});
+      if (st == 0) step(0, 2, (kt + 2) * GBK, 1, Y_{}, Y_{}, Y_{}, Y_{});
+      else if (st == 1) step(1, 0, (kt + 2) * GBK, 2, Y_{}, Y_{}, Y_{}, Y_{});
+      else step(2, 1, (kt + 2) * GBK, 0, Y_{}, Y_{}, Y_{}, Y_{});
     } else if (kt + 1 < nk) {
-      if (st == 0) step(0, 0, 0, 1, N_{}, Y_{}, N_{});
-      else if (st == 1) step(1, 0, 0, 2, N_{}, Y_{}, N_{});
-      else step(2, 0, 0, 0, N_{}, Y_{}, N_{});
+      if (st == 0) step(0, 0, 0, 1, N_{}, Y_{}, N_{}, N_{});
+      else if (st == 1) step(1, 0, 0, 2, N_{}, Y_{}, N_{}, N_{});
+      else step(2, 0, 0, 0, N_{}, Y_{}, N_{}, N_{});
     } else {
-      if (st == 0) step(0, 0, 0, 0, N_{}, N_{}, N_{});
-      else if (st == 1) step(1, 0, 0, 0, N_{}, N_{}, N_{});
-      else step(2, 0, 0, 0, N_{}, N_{}, N_{});
+      if (st == 0) step(0, 0, 0, 0, N_{}, N_{}, N_{}, N_{});
+      else if (st == 1) step(1, 0, 0, 0, N_{}, N_{}, N_{}, N_{});
+      else step(2, 0, 0, 0, N_{}, N_{}, N_{}, N_{});
     }
   }
   wait_vmcnt<0>();                                         // the zero tile of a one-tile K

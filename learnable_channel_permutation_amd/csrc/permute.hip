@@ -31,6 +31,8 @@ namespace lcp {
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f2bf(f); }
 
+typedef __attribute__((address_space(3))) void* perm_lds_t;
+
 template <int B, int MODE>
 struct PermGeom {
   static constexpr int KS = B / 16;              // K steps of 16 over a block
@@ -114,9 +116,18 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
     const int seg_end = min(t_end, (b + 1) * tpb);
     __syncthreads();                      // previous block's fragments no longer read
     if (gfrag != nullptr) {
+      // every 16-byte entry goes global -> LDS directly; all of a thread's
+      // copies are in flight at once and one wait covers them (entry counts
+      // are multiples of 64, so each wave copies whole 1 KB rows or none)
       const u32x4* src = gfrag + (size_t)b * G::NARR * G::FRAG;
-      u32x4* dst = reinterpret_cast<u32x4*>(lds);
-      for (int e = threadIdx.x; e < G::NARR * G::FRAG; e += G::THREADS) dst[e] = src[e];
+      constexpr int NE = G::NARR * G::FRAG, PER = (NE + G::THREADS - 1) / G::THREADS;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int e0 = k * G::THREADS + 64 * w;
+        if (e0 < NE)
+          __builtin_amdgcn_global_load_lds(src + e0 + l, (perm_lds_t)(lds + (size_t)e0 * 8), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));   // vmcnt(0)
     } else {
       perm_prep<B, MODE>(P, colscale, b, transposeP, lds);
     }

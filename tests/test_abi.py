@@ -153,6 +153,8 @@ def test_step_argument_validation():
     assert fwd(layer=_lay(L, 0, p, p, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL
     assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 0, 128, 32, 64)) == L.LCP_E_INVAL
     assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 1 << 20, 1 << 12, 32, 64)) == L.LCP_E_INVAL
+    assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 1 << 18, 1 << 12, 32, 64)) == L.LCP_E_INVAL   # bf16 W of 2^30
+    assert fwd(layer=_lay(L, p, p, p, p, L.LCP_BF16, 64, 1 << 12, 1 << 18, 64)) == L.LCP_E_INVAL   # bf16 X of 2^30
     assert bwd(layer=_lay(L, p, p, 0, p, L.LCP_BF16, 64, 128, 32, 64)) == L.LCP_E_INVAL   # bf16 needs Xt
     assert bwd(n=need - 256) == L.LCP_E_WORKSPACE
     # iters * B above LCP_MAX_ITERS_B (8192): unsupported, nothing enqueued
