@@ -434,6 +434,7 @@ static int check_spgemm(const void* vals, const uint32_t* meta, const void* Xp, 
                         const void* Y) {
   if (!vals || !meta || !Xp || !Y || T <= 0 || cout <= 0 || cin <= 0) return LCP_E_INVAL;
   if (cout % 32 || cin % 32 || !fits_i32(cout, cin) || !fits_i32(T, cin) || !fits_i32(T, cout)) return LCP_E_INVAL;
+  if (!fits_bf16_gemm(T, cin)) return LCP_E_INVAL;
   if (!aligned16(vals) || !aligned16(Xp) || !aligned16(Y) || ((uintptr_t)meta & 3u)) return LCP_E_INVAL;
   return LCP_OK;
 }

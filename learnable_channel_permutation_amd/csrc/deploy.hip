@@ -30,7 +30,6 @@ namespace lcp {
 
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* dep_lds_t;
-__device__ const u32x4 g_dep_zero[1] = {{0u, 0u, 0u, 0u}};
 
 // ---- packing -------------------------------------------------------------------
 // One thread per (fragment, lane): 16 permuted positions of one row.
@@ -168,24 +167,49 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
 
   // load o of this thread for K step ks into ring stage `stage`: o < 2 the
   // weight fragment f = 8 o + w (row group f / 2, 32-position half f % 2),
-  // o = 2 the position words of row group w, o > 2 activation chunks
-  auto issue_one = [&](int stage, int ks, int o) {
+  // o = 2 the position words of row group w, o > 2 activation chunks. The
+  // loads go through buffer resources: each lane's byte offset is fixed per
+  // tile and a K step moves only the scalar offset; row groups and tokens
+  // past the matrices, and (in a step that may be the last, TAIL) K chunks
+  // past cin or whole steps past the end, read zeros from an offset past the
+  // resource.
+  constexpr uint32_t OOB = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(vals), (short)0,
+                                                                    (int)(uint32_t)((size_t)RG * KF * 1024), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rMt = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(meta), (short)0,
+                                                                     (int)(uint32_t)((size_t)RG * NK * 256), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Xp), (short)0,
+                                                                    (int)(uint32_t)((size_t)T * cin * 2), 0x00020000);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t voffV[2], voffX[2], voffM;
+  int kchX[2];
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    const int f = 8 * o + w, rg = m0 / 32 + (f >> 1);
+    voffV[o] = (rg < RG) ? (uint32_t)((((size_t)rg * KF + (f & 1)) * 64 + l) * 16) : OOB;
+    const int c = (o * 8 + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
+    kchX[o] = ch * 8;
+    voffX[o] = (n0 + row < T) ? (uint32_t)(((size_t)(n0 + row) * cin + ch * 8) * 2) : OOB;
+  }
+  voffM = (m0 / 32 + w < RG) ? (uint32_t)(((size_t)(m0 / 32 + w) * NK * 64 + l) * 4) : OOB;
+  auto issue_one = [&](int stage, int ks, int o, auto TAIL) {
     unsigned char* sb = sp_lds + stage * SP_STAGE;
+    constexpr bool TL = decltype(TAIL)::value;
     if (o < 2) {
-      const int f = 8 * o + w, rg = m0 / 32 + (f >> 1), kf = 2 * ks + (f & 1);
-      const void* src = (rg < RG && kf < KF) ? (const void*)(vals + ((size_t)rg * KF + kf) * 64 + l)
-                                             : (const void*)g_dep_zero;
-      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + f * 1024), 16, 0, 0);
+      uint32_t vo = voffV[o];
+      if (TL && 2 * ks + (wu & 1) >= KF) vo = OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (dep_lds_t)(sb + (8 * o + wu) * 1024), 16, (int)vo,
+                                               (int)((uint32_t)ks * 2048u), 0, 0);
     } else if (o == 2) {
-      const int rg = m0 / 32 + w;
-      const void* src = (rg < RG && ks < NK) ? (const void*)(meta + ((size_t)rg * NK + ks) * 64 + l)
-                                             : (const void*)g_dep_zero;
-      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_MOFF + w * 256), 4, 0, 0);
+      uint32_t vo = voffM;
+      if (TL && ks >= NK) vo = OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rMt, (dep_lds_t)(sb + SP_MOFF + wu * 256), 4, (int)vo,
+                                               (int)((uint32_t)ks * 256u), 0, 0);
     } else {
-      const int c = ((o - 3) * 8 + w) * 64 + l, row = c >> 3, ch = (c & 7) ^ ((row >> 1) & 7);
-      const int gn = n0 + row, gk = ks * 64 + ch * 8;
-      const void* src = (gn < T && gk < cin) ? (const void*)(Xp + (size_t)gn * cin + gk) : (const void*)g_dep_zero;
-      __builtin_amdgcn_global_load_lds(src, (dep_lds_t)(sb + SP_BOFF + ((o - 3) * 8 + w) * 1024), 16, 0, 0);
+      uint32_t vo = voffX[o - 3];
+      if (TL && ks * 64 + kchX[o - 3] >= cin) vo = OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (dep_lds_t)(sb + SP_BOFF + ((o - 3) * 8 + wu) * 1024), 16, (int)vo,
+                                               (int)((uint32_t)ks * 128u), 0, 0);
     }
   };
 
@@ -232,7 +256,7 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
   // the tile of K step ks goes to stage `lstage`; with `next` the first
   // fragments of stage `nstage` are read after the barrier. WAIT (steady
   // state): the loads of the RS - 2 tiles after the next one may stay in flight.
-  auto step = [&](int stage, int lstage, int ks, int nstage, bool load, bool next, auto WAIT) {
+  auto step = [&](int stage, int lstage, int ks, int nstage, bool load, bool next, auto WAIT, auto TAIL) {
     __builtin_amdgcn_s_waitcnt(0xC07F);                    // sub-step 0's fragments are in
     __builtin_amdgcn_sched_barrier(0);
     rd(stage, 1);
@@ -242,7 +266,7 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
       for (int o = 0; o < NL; ++o)
         if (load && o * NM / NL == m) {
           __builtin_amdgcn_sched_barrier(0);
-          issue_one(lstage, ks, o);
+          issue_one(lstage, ks, o, TAIL);
           __builtin_amdgcn_sched_barrier(0);
         }
       mma(0, m);
@@ -264,19 +288,21 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
 #pragma unroll
   for (int s = 0; s < RS - 1; ++s)
 #pragma unroll
-    for (int o = 0; o < NL; ++o) issue_one(s, s, o);
+    for (int o = 0; o < NL; ++o) issue_one(s, s, o, std::true_type{});
   sp_wait_vmcnt<(RS - 2) * NL>();
   __builtin_amdgcn_s_barrier();
   rd(0, 0);
   int kt = 0;
-  for (; kt + 2 * RS - 2 < NK; kt += RS) {                 // RS steady-state steps
+  // RS steady-state steps; they load K steps up to kt + 2 RS - 2 < NK - 1,
+  // never the last one
+  for (; kt + 2 * RS - 1 < NK; kt += RS) {
 #pragma unroll
     for (int s = 0; s < RS; ++s)
-      step(s, (s + RS - 1) % RS, kt + s + RS - 1, (s + 1) % RS, true, true, std::true_type{});
+      step(s, (s + RS - 1) % RS, kt + s + RS - 1, (s + 1) % RS, true, true, std::true_type{}, std::false_type{});
   }
   for (; kt < NK; ++kt)                                    // the last steps, all loads retired at each barrier
     step(kt % RS, (kt + RS - 1) % RS, kt + RS - 1, (kt + 1) % RS, kt + RS - 1 < NK, kt + 1 < NK,
-         std::false_type{});
+         std::false_type{}, std::true_type{});
   sp_wait_vmcnt<0>();                                      // the zero tiles of a short K
 
   // lane (h, ln) of block (i, j): token n0 + wn*64 + 32j + ln, rows
