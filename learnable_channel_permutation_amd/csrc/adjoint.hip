@@ -39,7 +39,7 @@
 namespace lcp {
 
 typedef __attribute__((address_space(3))) void* adj_lds_t;
-__device__ const u32x4 g_adj_zero[1] = {{0u, 0u, 0u, 0u}};
+constexpr uint32_t kAdjOOB = 0x80000000u;   // a buffer offset past every operand (reads zeros)
 
 template <int B>
 struct AdjGeom {
@@ -116,6 +116,14 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
   const int t_begin = blockIdx.x * tpw;
   const int t_end = min(total, t_begin + tpw);
   const int first_b = t_begin / tpb;
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), (short)0,
+                                                                    (int)(uint32_t)((size_t)cout * cin * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(G), (short)0,
+                                                                    (int)(uint32_t)((size_t)cout * cin * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rBits = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(bits), (short)0, (int)(uint32_t)((size_t)(cin / B) * cout * TT * 4), 0x00020000);
+  const uint32_t vw_lane = (uint32_t)(((size_t)lrow * cin + 8 * h) * 2);   // W / G element (lrow, 8h) of a tile
+  const uint32_t vb_lane = (uint32_t)((n * TT + h) * 4);                    // mask word h of tile row n
 
   for (int seg = t_begin; seg < t_end;) {
     const int b = seg / tpb;
@@ -156,29 +164,30 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
 
     // the load instructions of one tile into stage st (with WS waves sharing a
     // ring, wave `half` issues every WS-th of them)
+    // loads through buffer resources: a lane's offset inside a tile is fixed
+    // (row lrow, or n for the mask words), the tile and block move only the
+    // scalar offset, rows past cout read zeros (offset past the resource)
     auto issue = [&](int st, int tile) {
       unsigned char* sb = ring + st * STAGE;
       const int i0 = (tile - b * tpb) * 32;
-      const int i = i0 + lrow;
+      const uint32_t vw = (i0 + lrow < cout) ? vw_lane : kAdjOOB;
+      const uint32_t vb = (i0 + n < cout) ? vb_lane : kAdjOOB;
+      const uint32_t sw0 = (uint32_t)(((size_t)i0 * cin + b * B) * 2);
 #pragma unroll
       for (int p = 0; p < KS; ++p) {
         if (p % WS != half) continue;
-        const size_t o = (size_t)i * cin + b * B + 16 * p + 8 * h;
-        const void* sw = (i < cout) ? (const void*)(W + o) : (const void*)g_adj_zero;
-        const void* sg = (i < cout) ? (const void*)(G + o) : (const void*)g_adj_zero;
-        __builtin_amdgcn_global_load_lds(sw, (adj_lds_t)(sb + p * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(sg, (adj_lds_t)(sb + (KS + p) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (adj_lds_t)(sb + p * 1024), 16, (int)vw, (int)(sw0 + 32 * p), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, (adj_lds_t)(sb + (KS + p) * 1024), 16, (int)vw, (int)(sw0 + 32 * p),
+                                                 0, 0);
       }
       // mask words (block-major [block][row][TT]): instruction q, lane (h, n)
       // -> word 2q + h of row i0 + n, all inside the tile's 32 * TT words
+      const uint32_t sb0 = (uint32_t)(((size_t)b * cout + i0) * TT * 4);
 #pragma unroll
       for (int q = 0; q < Gm::BI; ++q) {
         if (q % WS != half) continue;
-        const int a = (2 * q + h) % TT;
-        const int ib = i0 + n;
-        const void* sbits = (ib < cout) ? (const void*)(bits + ((size_t)b * cout + ib) * TT + a)
-                                        : (const void*)g_adj_zero;
-        __builtin_amdgcn_global_load_lds(sbits, (adj_lds_t)(sb + 2 * KS * 1024 + q * 256), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rBits, (adj_lds_t)(sb + 2 * KS * 1024 + q * 256), 4,
+                                                 (int)(vb + 4 * ((2 * q + h) % TT - h)), (int)sb0, 0, 0);
       }
     };
 
