@@ -27,10 +27,11 @@
 //   dP^T[k][j] += sum_i (W_hat . Y)[i][k] S[i][j],  S[i][j] = |W[i][j]| n_j,
 // which is S_b^T ((G_b P_b) . (W_b P_b)): the gradient reaching the 0/1 mask,
 // dE/dM = (G_b P_b) . W_hat_b, handed unchanged to S_hat_b = S_b P_b.
-// For B = 128 the four waves of a workgroup take the same 32-row tile, share
-// one four-stage ring (each wave issues a quarter of the loads, a barrier per
-// tile) and each owns one 32-wide block of positions k: it forms W_hat and Y
-// for its own positions only and transposes all of G and W; for B <= 64
+// For B = 128 a workgroup has eight waves in two slots; the four waves of a
+// slot take the same 32-row tile, share one three-stage ring (each wave
+// issues a quarter of the loads, a barrier per tile) and each owns one 32-wide
+// block of positions k: it forms W_hat and Y for its own positions only and
+// transposes all of G and W, one source column block at a time; for B <= 64
 // every wave owns whole tiles and its own ring. Partial sums of waves owning
 // the same entries are added through LDS in a fixed order.
 #include "common.h"
@@ -47,12 +48,15 @@ struct AdjGeom {
   static constexpr int TT = B / 32;             // 32-wide column blocks
   static constexpr int WS = (B == 128) ? 4 : 1; // waves sharing one row tile
   static constexpr int NA = TT / WS;            // position blocks (a) owned per wave
-  static constexpr int TILES = 4 / WS;          // row tiles in flight per workgroup
+  // B = 128: eight waves, two row tiles (slots) of four waves each, so every
+  // SIMD runs two waves; B <= 64: four waves, one row tile each
+  static constexpr int WAVES = (B == 128) ? 8 : 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TILES = WAVES / WS;      // row tiles in flight per workgroup
   static constexpr int ROWS = 32 * TILES;       // rows per workgroup step
   static constexpr int FRAG = TT * KS * 64;     // u32x4 entries of the P fragments
-  // ring stages: B = 128 keeps one row tile per workgroup, so a deeper ring
-  // gives the CU enough bytes in flight to stream at HBM rate
-  static constexpr int S = (B == 128) ? 4 : 2;
+  // ring stages: a shared B = 128 ring is one stage deeper
+  static constexpr int S = (B == 128) ? 3 : 2;
   static constexpr int BI = (TT + 1) / 2;       // mask-word load instructions per tile
   static constexpr int STAGE = 2 * KS * 1024 + BI * 256;   // bytes per stage
   static constexpr int IPT = 2 * KS + BI;       // load instructions per tile
@@ -89,7 +93,7 @@ __device__ __forceinline__ u32x4 identity_slots(int v, int h, int n) {
 // spans at most `maxseg` blocks; it writes one partial B x B matrix per block
 // segment to part[(g * maxseg + k) * B * B] (k = block - first block of g).
 template <int B, bool STE>
-__global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
+__global__ __launch_bounds__(AdjGeom<B>::THREADS, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ W, const u32x4* __restrict__ gfrag,
     const float* __restrict__ P, const uint32_t* __restrict__ bits, int cout, int cin, int tpw,
     int maxseg, const float* __restrict__ ste_norms, float* __restrict__ part) {
@@ -135,16 +139,16 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
       // global -> LDS directly, all of a thread's copies in flight at once
       // (FRAG is a multiple of 64: each wave copies whole 1 KB rows or none)
       const u32x4* src = gfrag + (size_t)b * Gm::FRAG;
-      constexpr int PER = (Gm::FRAG + 255) / 256;
+      constexpr int PER = (Gm::FRAG + Gm::THREADS - 1) / Gm::THREADS;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
-        const int e0 = k * 256 + 64 * w;
+        const int e0 = k * Gm::THREADS + 64 * w;
         if (e0 < Gm::FRAG) __builtin_amdgcn_global_load_lds(src + e0 + l, (adj_lds_t)(fb + (size_t)e0 * 8), 16, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));   // vmcnt(0)
     } else {
       const float* src = P + (size_t)b * B * B;
-      for (int e_idx = t; e_idx < B * B; e_idx += 256) {
+      for (int e_idx = t; e_idx < B * B; e_idx += Gm::THREADS) {
         const int j = e_idx / B, k = e_idx % B;
         const int tt = k >> 5, nn = k & 31, p = j >> 4, hh = (j >> 3) & 1, e = j & 7;
         fb[(((tt * KS + p) * 64) + 32 * hh + nn) * 8 + e] = (uint16_t)f2bf(src[e_idx]);
@@ -193,57 +197,58 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
 
     const int first = seg + slot;
     const int ntile = (first < seg_end) ? (seg_end - first + TILES - 1) / TILES : 0;
+    // every wave runs the first slot's count of iterations (the barrier of a
+    // shared ring needs all of them); a slot with one tile fewer idles
+    // through its last one
+    const int nit = (seg_end - seg + TILES - 1) / TILES;
     // loads this wave issues per tile (the waves of a shared ring split them)
     const int nload = 2 * (KS / WS) + (WS == 1 ? Gm::BI : (half < Gm::BI ? 1 : 0));
 #pragma unroll
     for (int q = 0; q < S - 1; ++q)
       if (q < ntile) issue(q, first + q * TILES);
-    for (int it = 0; it < ntile; ++it) {
+    for (int it = 0; it < (WS > 1 ? nit : ntile); ++it) {
       // this wave's loads of tile `it` have landed (only later tiles' loads,
       // issued after them, may still be in flight); the stage refilled below
       // was consumed in the previous iteration. A shared ring also needs every
       // wave's part and every wave done with that stage: one barrier.
-      const int later = min(S - 2, ntile - 1 - it);
+      const int later = max(0, min(S - 2, ntile - 1 - it));
       if (S == 2) __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
       else adj_wait_vm(later * nload);
       if (WS > 1) __builtin_amdgcn_s_barrier();
+      if (it >= ntile) continue;                     // idle slot (shared ring only)
       if (it + S - 1 < ntile) issue((it + S - 1) % S, first + (it + S - 1) * TILES);
       const unsigned char* sb = ring + (it % S) * STAGE;
       const u32x4* LW = reinterpret_cast<const u32x4*>(sb);
       const u32x4* LG = reinterpret_cast<const u32x4*>(sb + KS * 1024);
       const uint32_t* LB = reinterpret_cast<const uint32_t*>(sb + 2 * KS * 1024);
 
-      // transposed G and W (and S = |W| n_j) for all column blocks of the
-      // source channels j: 16 rows per lane
-      u32x4 gT[TT][2], wT[TT][2], sT[TT][2];
-#pragma unroll
-      for (int o = 0; o < TT; ++o) {
-        const int t2 = o;
+      // G and W (and S = |W| n_j) of source column block o transposed into
+      // the "16 rows per lane" layout (MFMA against the identity, exact)
+      auto transpose_block = [&](int o, u32x4 (&gT)[2], u32x4 (&wT)[2], u32x4 (&sT)[2]) {
         floatx16 tg = {}, tw = {};
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
           const u32x4 id = identity_slots(v, h, n);
-          tg = mfma32(LG[(2 * t2 + v) * 64 + l], id, tg);
-          tw = mfma32(LW[(2 * t2 + v) * 64 + l], id, tw);
+          tg = mfma32(LG[(2 * o + v) * 64 + l], id, tg);
+          tw = mfma32(LW[(2 * o + v) * 64 + l], id, tw);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          gT[o][u] = u32x4{pack2_exact(tg[8 * u], tg[8 * u + 1]), pack2_exact(tg[8 * u + 2], tg[8 * u + 3]),
-                           pack2_exact(tg[8 * u + 4], tg[8 * u + 5]), pack2_exact(tg[8 * u + 6], tg[8 * u + 7])};
-          wT[o][u] = u32x4{pack2_exact(tw[8 * u], tw[8 * u + 1]), pack2_exact(tw[8 * u + 2], tw[8 * u + 3]),
-                           pack2_exact(tw[8 * u + 4], tw[8 * u + 5]), pack2_exact(tw[8 * u + 6], tw[8 * u + 7])};
+          gT[u] = u32x4{pack2_exact(tg[8 * u], tg[8 * u + 1]), pack2_exact(tg[8 * u + 2], tg[8 * u + 3]),
+                        pack2_exact(tg[8 * u + 4], tg[8 * u + 5]), pack2_exact(tg[8 * u + 6], tg[8 * u + 7])};
+          wT[u] = u32x4{pack2_exact(tw[8 * u], tw[8 * u + 1]), pack2_exact(tw[8 * u + 2], tw[8 * u + 3]),
+                        pack2_exact(tw[8 * u + 4], tw[8 * u + 5]), pack2_exact(tw[8 * u + 6], tw[8 * u + 7])};
           if (STE) {
             float sv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) sv[e] = __builtin_fabsf(tw[8 * u + e]) * nrm[o];
-            sT[o][u] = u32x4{pack2(sv[0], sv[1]), pack2(sv[2], sv[3]), pack2(sv[4], sv[5]), pack2(sv[6], sv[7])};
+            sT[u] = u32x4{pack2(sv[0], sv[1]), pack2(sv[2], sv[3]), pack2(sv[4], sv[5]), pack2(sv[6], sv[7])};
           }
         }
-      }
-#pragma unroll
-      for (int ai = 0; ai < NA; ++ai) {
-        const int a = half * NA + ai;
-        // W_hat and Y for positions 32a + n, rows 16h + r
+      };
+      // W_hat = W P_b and Y = G P_b for positions 32a + n (rows 16h + r),
+      // masked and packed as MFMA A operands (and W_hat . Y unmasked for STE)
+      auto position_block = [&](int a, u32x4 (&aop)[2], u32x4 (&yop)[2], u32x4 (&qop)[2]) {
         floatx16 wh = {}, yy = {};
 #pragma unroll
         for (int p = 0; p < KS; ++p) {
@@ -259,7 +264,6 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
           const u32x4 v4 = mw[q];
           m16[4 * q] = v4.x; m16[4 * q + 1] = v4.y; m16[4 * q + 2] = v4.z; m16[4 * q + 3] = v4.w;
         }
-        u32x4 aop[2], yop[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           float av[8], yv[8];
@@ -271,28 +275,50 @@ __global__ __launch_bounds__(256, (B == 128) ? 1 : 2) void adjoint_bf16_kernel(
           }
           aop[u] = u32x4{pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7])};
           yop[u] = u32x4{pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]), pack2(yv[6], yv[7])};
-        }
-#pragma unroll
-        for (int o = 0; o < TT; ++o)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            acc[ai][o] = mfma32(aop[u], gT[o][u], acc[ai][o]);
-            acc[ai][o] = mfma32(yop[u], wT[o][u], acc[ai][o]);
-          }
-        if (STE) {
-          // (W_hat . Y), unmasked
-          u32x4 qop[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          if (STE) {
             float qv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) qv[e] = wh[8 * u + e] * yy[8 * u + e];
             qop[u] = u32x4{pack2(qv[0], qv[1]), pack2(qv[2], qv[3]), pack2(qv[4], qv[5]), pack2(qv[6], qv[7])};
           }
+        }
+      };
+      // dP^T[k][j] += sum_i A[i][k] G[i][j] + (Y . M)[i][k] W[i][j] (+ STE term)
+      auto accumulate = [&](floatx16& c, const u32x4 (&aop)[2], const u32x4 (&yop)[2], const u32x4 (&qop)[2],
+                            const u32x4 (&gT)[2], const u32x4 (&wT)[2], const u32x4 (&sT)[2]) {
 #pragma unroll
-          for (int o = 0; o < TT; ++o)
+        for (int u = 0; u < 2; ++u) {
+          c = mfma32(aop[u], gT[u], c);
+          c = mfma32(yop[u], wT[u], c);
+        }
+        if (STE) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) acc[ai][o] = mfma32(qop[u], sT[o][u], acc[ai][o]);
+          for (int u = 0; u < 2; ++u) c = mfma32(qop[u], sT[u], c);
+        }
+      };
+      if constexpr (NA > 1) {
+        // every wave owns all positions: transpose once, then each position block
+        u32x4 gT[TT][2], wT[TT][2], sT[TT][2];
+#pragma unroll
+        for (int o = 0; o < TT; ++o) transpose_block(o, gT[o], wT[o], sT[o]);
+#pragma unroll
+        for (int ai = 0; ai < NA; ++ai) {
+          u32x4 aop[2], yop[2], qop[2];
+          position_block(half * NA + ai, aop, yop, qop);
+#pragma unroll
+          for (int o = 0; o < TT; ++o) accumulate(acc[ai][o], aop, yop, qop, gT[o], wT[o], sT[o]);
+        }
+      } else {
+        // one position block per wave: its operands first, then each source
+        // column block transposed just before its multiply-adds (fewer live
+        // registers; no transpose is repeated)
+        u32x4 aop[2], yop[2], qop[2];
+        position_block(half, aop, yop, qop);
+#pragma unroll
+        for (int o = 0; o < TT; ++o) {
+          u32x4 gT[2], wT[2], sT[2];
+          transpose_block(o, gT, wT, sT);
+          accumulate(acc[0][o], aop, yop, qop, gT, wT, sT);
         }
       }
     }
@@ -439,7 +465,7 @@ AdjSplit adjoint_split(int cout, int cin, int B) {
 template <int B, bool STE>
 static void adj_bf16(const uint16_t* G, const uint16_t* W, const u32x4* gfrag, const float* P, const uint32_t* bits,
                      int cout, int cin, const AdjSplit& sp, const float* nrm, float* part, hipStream_t s) {
-  adjoint_bf16_kernel<B, STE><<<sp.grid, 256, adj_lds_bytes<B>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw,
+  adjoint_bf16_kernel<B, STE><<<sp.grid, AdjGeom<B>::THREADS, adj_lds_bytes<B>(), s>>>(G, W, gfrag, P, bits, cout, cin, sp.tpw,
                                                                       sp.maxseg, nrm, part);
 }
 
