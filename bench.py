@@ -157,7 +157,10 @@ def attainable_peaks(torch, spec):
     """Measured-attainable denominators on this GPU, in this process: a plain
     device copy (torch's copy kernel, 1 GiB read + 1 GiB written) and
     hipBLASLt (torch.matmul) on the two GEMM shapes of the step with random
-    bf16 operands. Each is the best of 3 rounds of 10 timed calls."""
+    bf16 operands. The step holds X both as [T, Cin] and as its transpose, so
+    each product is timed with the right operand in either layout and the
+    faster one is kept (hipBLASLt's speed depends on it). Each is the best of
+    3 rounds of 10 timed calls."""
     dev = torch.device("cuda:0")
     out = {}
     n = (1 << 30) // 4
@@ -190,8 +193,13 @@ def attainable_peaks(torch, spec):
     D = torch.randn((cout, cin), device=dev, generator=g).to(torch.bfloat16)
     Xt = X.t().contiguous()
     flops = 2.0 * cout * cin * T
-    ms_dd = best(lambda: torch.matmul(R, X))
-    ms_err = best(lambda: torch.matmul(D, Xt))
+    # dD: G = R X with X as stored ([T, Cin]) or as the transposed copy's view;
+    # error: R = D Xᵀ with X's view (K contiguous in both) or the copy itself.
+    dd = {"nn": best(lambda: torch.matmul(R, X)), "nt": best(lambda: torch.matmul(R, Xt.t()))}
+    er = {"nt": best(lambda: torch.matmul(D, X.t())), "nn": best(lambda: torch.matmul(D, Xt))}
+    lay_dd, ms_dd = min(dd.items(), key=lambda kv: kv[1])
+    lay_err, ms_err = min(er.items(), key=lambda kv: kv[1])
+    out["hipblaslt_layouts"] = {"dD": lay_dd, "error": lay_err}
     out["hipblaslt_dD_TFLOP_per_s"] = round(flops / (ms_dd * 1e-3) / 1e12, 1)
     out["hipblaslt_error_TFLOP_per_s"] = round(flops / (ms_err * 1e-3) / 1e12, 1)
     out["hipblaslt_dD_us"] = round(ms_dd * 1e3, 1)
