@@ -420,21 +420,23 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
     auto slot = [&](int gg) {
       return dP + ((size_t)gg * seg_maxseg + (b - (gg * seg_tpw) / seg_tpb)) * B * B;
     };
-    float cur[4][CPL];
-    ld_block<B>(slot(g_lo), cur, w, lr, lc);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) d[a][c] = 0.f;
-    for (int gg = g_lo; gg <= g_hi; ++gg) {
-      float nxt[4][CPL];
-      if (gg < g_hi) ld_block<B>(slot(gg + 1), nxt, w, lr, lc);
+    // up to four partials in flight at once, added in workgroup order
+    for (int g0 = g_lo; g0 <= g_hi; g0 += 4) {
+      float q[4][4][CPL];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int k = 0; k < 4; ++k)
+        if (g0 + k <= g_hi) ld_block<B>(slot(g0 + k), q[k], w, lr, lc);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          d[a][c] += cur[a][c];
-          cur[a][c] = (gg < g_hi) ? nxt[a][c] : 0.f;
+      for (int k = 0; k < 4; ++k)
+        if (g0 + k <= g_hi) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) d[a][c] += q[k][a][c];
         }
     }
   }
