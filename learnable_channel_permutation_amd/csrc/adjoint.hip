@@ -77,12 +77,13 @@ __device__ __forceinline__ void adj_wait_vm(int n) {
 }
 
 __device__ __forceinline__ u32x4 identity_slots(int v, int h, int n) {
-  // MFMA B operand of the 32 x 32 identity, K step v: slot e of lane (h, n)
-  // is 1 when column n equals row 16v + 8h + e
+  // MFMA B operand of the 32 x 32 identity, K step v of a 32-column group:
+  // slot e of lane (h, n) stands for column 16h + 8v + e of the group and is
+  // 1 when that equals n
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int e0 = 16 * v + 8 * h + 2 * q;
+    const int e0 = 16 * h + 8 * v + 2 * q;
     w[q] = (e0 == n ? 0x3f80u : 0u) | ((e0 + 1 == n ? 0x3f80u : 0u) << 16);
   }
   return u32x4{w[0], w[1], w[2], w[3]};
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(AdjGeom<B>::THREADS, (B == 128) ? 1 : 2) void adjoi
                                                                     (int)(uint32_t)((size_t)cout * cin * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rBits = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(bits), (short)0, (int)(uint32_t)((size_t)(cin / B) * cout * TT * 4), 0x00020000);
-  const uint32_t vw_lane = (uint32_t)(((size_t)lrow * cin + 8 * h) * 2);   // W / G element (lrow, 8h) of a tile
+  const uint32_t vw_lane = (uint32_t)(((size_t)lrow * cin + 16 * h) * 2);  // W / G element (lrow, 16h) of a tile
   const uint32_t vb_lane = (uint32_t)((n * TT + h) * 4);                    // mask word h of tile row n
 
   for (int seg = t_begin; seg < t_end;) {
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(AdjGeom<B>::THREADS, (B == 128) ? 1 : 2) void adjoi
     const int seg_end = min(t_end, (b + 1) * tpb);
     __syncthreads();                       // fragments and sums of the previous block consumed
     // P fragments (MFMA B operand, K = source channel j, N = position k):
-    // F[(t*KS + p)*64 + lane][e] = P_b[16p + 8h + e][32t + n]
+    // F[(t*KS + p)*64 + lane][e] = P_b[32(p/2) + 16h + 8(p%2) + e][32t + n]
     if (gfrag != nullptr) {
       // global -> LDS directly, all of a thread's copies in flight at once
       // (FRAG is a multiple of 64: each wave copies whole 1 KB rows or none)
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(AdjGeom<B>::THREADS, (B == 128) ? 1 : 2) void adjoi
       const float* src = P + (size_t)b * B * B;
       for (int e_idx = t; e_idx < B * B; e_idx += Gm::THREADS) {
         const int j = e_idx / B, k = e_idx % B;
-        const int tt = k >> 5, nn = k & 31, p = j >> 4, hh = (j >> 3) & 1, e = j & 7;
+        const int tt = k >> 5, nn = k & 31, p = 2 * (j >> 5) + ((j >> 3) & 1), hh = (j >> 4) & 1, e = j & 7;
         fb[(((tt * KS + p) * 64) + 32 * hh + nn) * 8 + e] = (uint16_t)f2bf(src[e_idx]);
       }
     }
@@ -180,9 +181,10 @@ __global__ __launch_bounds__(AdjGeom<B>::THREADS, (B == 128) ? 1 : 2) void adjoi
 #pragma unroll
       for (int p = 0; p < KS; ++p) {
         if (p % WS != half) continue;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (adj_lds_t)(sb + p * 1024), 16, (int)vw, (int)(sw0 + 32 * p), 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, (adj_lds_t)(sb + (KS + p) * 1024), 16, (int)vw, (int)(sw0 + 32 * p),
-                                                 0, 0);
+        // K step p: channels 32(p/2) + 16h + 8(p%2) + e of the block
+        const uint32_t sp = sw0 + 2 * (32 * (p >> 1) + 8 * (p & 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (adj_lds_t)(sb + p * 1024), 16, (int)vw, (int)sp, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, (adj_lds_t)(sb + (KS + p) * 1024), 16, (int)vw, (int)sp, 0, 0);
       }
       // mask words (block-major [block][row][TT]): instruction q, lane (h, n)
       // -> word 2q + h of row i0 + n, all inside the tile's 32 * TT words

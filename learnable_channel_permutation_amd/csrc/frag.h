@@ -11,7 +11,8 @@
 // with lane = 32h + rho and, for F1/FQ, K step p = 2 t2 + u covering
 // j = 32 t2 + 16h + 8u + e; for F2, p = 2t + u covering k = 32t + 16h + 8u + e.
 // Adjoint set, per block (see adjoint.hip):
-//   FB[t][p][lane]      Pb[16p + 8h + e][32t + n]     (lane = 32h + n)
+//   FB[t][p][lane]      Pb[j][32t + n]   (lane = 32h + n), K step p covering
+//                       j = 32(p/2) + 16h + 8(p%2) + e as in F1
 #pragma once
 
 #include "common.h"
@@ -93,12 +94,13 @@ __device__ __forceinline__ void frag_build(const float* Ps, const float* ns, u32
       }
       fo[(1 + NSPLIT) * FRAG + ent] = pack8(v);
     }
-    // FB (adjoint): Pb[16p + 8h + e][32t + rho]
+    // FB (adjoint): Pb[jb + e][32t + rho], the K slots of F1
     {
       const int k = 32 * t + rho;
+      const int jb = 32 * (p >> 1) + half;
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = Ps[(16 * p + 8 * h + e) * PP + k];
+      for (int e = 0; e < 8; ++e) v[e] = Ps[(jb + e) * PP + k];
       ao[ent] = pack8(v);
     }
   }
