@@ -127,7 +127,9 @@ typedef struct lcp_cfg {
  * Forward kernels: 0 Sinkhorn, 1 permute+mask+unpermute, 2 error GEMM,
  * 3 error (or cosine) finalisation, 4 hardening (harden = 1 only). Backward
  * kernels: 0 dD GEMM, 1 block adjoint, 2 Sinkhorn adjoint, 3 cosine
- * gradient dL/dY~ (cosine objective only). */
+ * gradient dL/dY~ (cosine objective only). For BF16 layers with B = 64 and
+ * mask_ste = 0 the block adjoint runs inside the dD GEMM's epilogue: kernel 0
+ * is then both, and nothing runs between start[1] and stop[1]. */
 typedef struct lcp_timing {
   void* start[8];
   void* stop[8];

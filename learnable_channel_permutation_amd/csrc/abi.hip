@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/lcp.h"
@@ -54,7 +55,11 @@ StepLayout step_layout(int cout, int cin, int T, int B, int iters, lcp_dtype dt)
   L.party = o; o += align_up((size_t)L.nparts * 4);
   L.E = o;     o += align_up(4 * 4);    // E, dD factor, cosine coefficients of Y and R
   L.GY = o;    o += align_up((size_t)cout * L.pitch * esize(dt));   // cosine dL/dY~
-  L.adj = o;   o += align_up((size_t)L.sp.grid * L.sp.maxseg * B * B * 4);
+  // block adjoint partials: (workgroup, segment) slots, or one per (row panel,
+  // block) when the adjoint is fused into the dD GEMM (bf16, B = 64)
+  const size_t adj_slots = std::max((size_t)L.sp.grid * L.sp.maxseg,
+                                    bf && B == 64 ? (size_t)dd_adjoint_panels(cout) * L.nb : (size_t)0);
+  L.adj = o;   o += align_up(adj_slots * B * B * 4);
   L.fragF = o; o += bf ? align_up((size_t)L.nb * frag_fwd_entries(B) * 16) : 0;
   L.fragA = o; o += bf ? align_up((size_t)L.nb * frag_adj_entries(B) * 16) : 0;
   L.total = o;
@@ -152,6 +157,22 @@ static int step_bwd_impl(const lcp_layer* L, const float* logits, const lcp_cfg*
     R = GY;
   }
   const float* ste = c->mask_ste ? L->norms : nullptr;
+  const u32x4* fragA = (const u32x4*)(base + Ly.fragA);
+  if (bf && L->B == 64 && !c->mask_ste) {
+    // the block adjoint taken in the dD GEMM's epilogue (G is never stored);
+    // the Sinkhorn adjoint adds the row-panel partials in panel order
+    tmr.start(0);
+    LCP_RUN(launch_gemm_dd_adjoint_bf16((const uint16_t*)R, Ly.pitch, (const uint16_t*)L->Xt, Ly.pitch, L->cout,
+                                        L->cin, Ly.pitch, Ews, (const uint16_t*)L->W, fragA, bits, adj, s));
+    tmr.stop(0);
+    tmr.start(1);
+    tmr.stop(1);
+    const AdjSplit panels{dd_adjoint_panels(L->cout), -1, 0, 0};
+    tmr.start(2);
+    LCP_RUN(launch_sinkhorn_bwd(logits, adj, &panels, off, dlogits, Ly.nb, L->B, c->iters, c->tau, opt, s));
+    tmr.stop(2);
+    return LCP_OK;
+  }
   tmr.start(0);
   if (bf)
     LCP_RUN(launch_gemm_dd_bf16((const uint16_t*)R, Ly.pitch, (const uint16_t*)L->Xt, Ly.pitch, L->cout, L->cin,
@@ -160,7 +181,6 @@ static int step_bwd_impl(const lcp_layer* L, const float* logits, const lcp_cfg*
     LCP_RUN(launch_gemm_dd_f32((const float*)R, Ly.pitch, (const float*)L->X, L->cin, L->cout, L->cin, L->T, Ews,
                                (float*)Gd, L->cin, s));
   tmr.stop(0);
-  const u32x4* fragA = (const u32x4*)(base + Ly.fragA);
   tmr.start(1);
   if (bf)
     LCP_RUN(launch_adjoint_bf16((const uint16_t*)Gd, (const uint16_t*)L->W, fragA, P, bits, L->cout, L->cin,

@@ -1,5 +1,7 @@
 // Block adjoint of the LCP forward (mask held constant unless the
-// straight-through term below is on).
+// straight-through term below is on). The step uses these kernels for fp32
+// layers, B = 32 and 128, and the straight-through term; for bf16 layers
+// with B = 64 the dD GEMM computes the same sums in its epilogue (gemm.hip).
 //
 // Forward (per block b): W_hat_b = W_b P_b, A_b = W_hat_b . M_b,
 // W_tilde_b = A_b P_b^T. Given G = dL/dW_tilde (= -dL/dD), the chain rule gives

@@ -25,6 +25,9 @@
 //    sub-step reads the next one's fragments before its MFMAs.
 //  * gemm_err_kernel (the error product): a software-pipelined three-stage
 //    ring on 16x16x32 MFMAs, described at the kernel.
+//  * gemm_dd_kernel<..., ADJ = true>: the same backward product with the
+//    block adjoint of the LCP forward (B = 64) taken from the accumulators in
+//    the epilogue instead of storing G (dd_adjoint_epilogue).
 //
 // Epilogues: ERR stores C in bf16 and one sum of squares of the fp32
 // accumulators per workgroup (reduced later in a fixed order); ERRCOS also
@@ -84,11 +87,212 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// The backward product C = coef[1] * A B^T (bf16 out).
-template <int BM, int BN, int S, int LSP>
+// Fused block adjoint of the dD GEMM (ADJ, B = 64): arguments of the epilogue.
+struct DdAdj {
+  const uint16_t* W;     // [M][N] bf16, the layer weights
+  const u32x4* frag;     // [nb][FB entries] adjoint P fragments (frag.h)
+  const uint32_t* bits;  // [nb][M][2] mask words, block-major
+  float* part;           // [tiles_m][nb][64][64] partial dL/dP_b (row panel sums)
+  int nb;
+};
+constexpr int ADJ_B = 64, ADJ_FRAG = (ADJ_B / 32) * (ADJ_B / 16) * 64;   // u32x4 entries per block
+
+
+// Identity as an MFMA B operand for K step v of a 32-column group whose K
+// slot (h, e) stands for column 16h + 8v + e: slot e of lane (h, n) is 1 when
+// that column is n.
+__device__ __forceinline__ u32x4 dd_identity(int v, int h, int n) {
+  uint32_t r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e0 = 16 * h + 8 * v + 2 * q;
+    r[q] = (e0 == n ? 0x3f80u : 0u) | ((e0 + 1 == n ? 0x3f80u : 0u) << 16);
+  }
+  return u32x4{r[0], r[1], r[2], r[3]};
+}
+
+// Block adjoint from the dD accumulators (256 x 256 tile, B = 64). Wave
+// (wm, wn) holds G for rows m0 + 64wm + [0, 64) and the two whole blocks of
+// columns n0 + 128wn + [0, 128): lane (h, ln) of accumulator (i, j) has row
+// 32i + ln, columns 32j + 16h + r. Packed to bf16 (the values the unfused
+// path stores), eight of them are exactly the K slots of one MFMA A operand
+// whose slot (h, e) is column 32j + 16h + 8v + e: the channel order of the
+// adjoint fragments (frag.h), so G P_b needs no data movement. W is loaded in
+// the same layout. Per block and 32-row group:
+//   W_hat = W P_b, Y = G P_b (MFMA), masked -> A = W_hat . M, Y . M in bf16,
+//   G and W transposed per 32-column group by an MFMA against the identity,
+//   dP^T[k][j] += sum_i A[i][k] G[i][j] + (Y . M)[i][k] W[i][j].
+// The four row waves of a block are summed through LDS in wave order, and
+// the tile writes one partial per (row panel, block), which the Sinkhorn
+// adjoint adds in panel order. Rows past M contribute nothing (G zeroed, W
+// and the mask read as zeros).
+__device__ __forceinline__ void dd_adjoint_epilogue(floatx16 (&acc)[2][4], float scale, uint16_t* lds,
+                                                    const uint16_t* frag_lds, const DdAdj& adj, int M, int m0,
+                                                    int n0, int tm, int w, int l) {
+  const int wm = w / GWN, wn = w % GWN, h = l >> 5, ln = l & 31;
+  // G operands gA[i][j][v]: columns 32j + 16h + 8v + e of the wave's 128
+  u32x4 gA[2][4][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bool rv = m0 + 64 * wm + 32 * i + ln < M;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const floatx16& a = acc[i][j];
+        uint32_t q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          q[e] = rv ? pack2(a[8 * v + 2 * e] * scale, a[8 * v + 2 * e + 1] * scale) : 0u;
+        gA[i][j][v] = u32x4{q[0], q[1], q[2], q[3]};
+      }
+  }
+  __syncthreads();                                         // the ring is no longer read
+  // mask words of the wave's two blocks and 64 rows: [jb][row][2] in LDS
+  uint32_t* mw = reinterpret_cast<uint32_t*>(lds) + w * 256;
+  float* red = reinterpret_cast<float*>(lds) + 8 * 256;    // [wn][wm - 1][a, o][16][64]
+  const int bw0 = n0 / ADJ_B + 2 * wn;                     // first block of this wave
+  {
+    const int jb = l >> 5, c = l & 31;
+    const size_t rows = (size_t)adj.nb * M;                // words in bits: rows * 2
+    const size_t wi = ((size_t)(bw0 + jb) * M + m0 + 64 * wm) * 2 + 4 * c;
+    // one 8-byte load per row (a row's two words are 8-byte aligned, four of
+    // them need not be 16); rows past the array read zeros
+    uint2 v0 = uint2{0u, 0u}, v1 = uint2{0u, 0u};
+    if (wi + 2 <= rows * 2) v0 = *reinterpret_cast<const uint2*>(adj.bits + wi);
+    if (wi + 4 <= rows * 2) v1 = *reinterpret_cast<const uint2*>(adj.bits + wi + 2);
+    *reinterpret_cast<u32x4*>(mw + jb * 128 + 4 * c) = u32x4{v0.x, v0.y, v1.x, v1.y};
+  }
+  const u32x4* F0 = reinterpret_cast<const u32x4*>(frag_lds);
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int bidx = bw0 + jb;
+    const bool bvalid = bidx < adj.nb;                     // uniform over the wave
+    floatx16 cacc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int o = 0; o < 2; ++o) cacc[a][o] = floatx16{};
+    if (bvalid) {
+      const u32x4* F = F0 + (2 * wn + jb) * ADJ_FRAG;      // [a][p][lane]
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = m0 + 64 * wm + 32 * i + ln;
+        u32x4 wA[2][2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int v = 0; v < 2; ++v)
+            wA[o][v] = row < M ? *reinterpret_cast<const u32x4*>(adj.W + (size_t)row * (adj.nb * ADJ_B) + bidx * ADJ_B +
+                                                                 32 * o + 16 * h + 8 * v)
+                               : u32x4{0u, 0u, 0u, 0u};
+        // keep bits: bit r of km[a] for accumulator element r, row 32i + 8(r/4) + 4h + r%4, position 32a + ln
+        uint32_t km[2] = {0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(mw + jb * 128 + (32 * i + 8 * q + 4 * h) * 2);
+          const u32x4 x0 = src[0], x1 = src[1];            // rows +0, +1 | +2, +3, words (t = 0, 1)
+          const uint32_t wd[4][2] = {{x0.x, x0.y}, {x0.z, x0.w}, {x1.x, x1.y}, {x1.z, x1.w}};
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) km[a] |= ((wd[b][a] >> ln) & 1u) << (4 * q + b);
+        }
+        u32x4 aop[2][2], yop[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          floatx16 wh = {}, yy = {};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const u32x4 fp = F[(a * 4 + p) * 64 + l];
+            wh = mfma32(wA[p >> 1][p & 1], fp, wh);
+            yy = mfma32(gA[i][2 * jb + (p >> 1)][p & 1], fp, yy);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float av[8], yv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const bool keep = (km[a] >> (8 * u + e)) & 1u;
+              av[e] = keep ? wh[8 * u + e] : 0.f;
+              yv[e] = keep ? yy[8 * u + e] : 0.f;
+            }
+            aop[a][u] = u32x4{pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7])};
+            yop[a][u] = u32x4{pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]), pack2(yv[6], yv[7])};
+          }
+        }
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          floatx16 tg = {}, tw = {};
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const u32x4 id = dd_identity(v, h, ln);
+            tg = mfma32(gA[i][2 * jb + o][v], id, tg);
+            tw = mfma32(wA[o][v], id, tw);
+          }
+          u32x4 gT[2], wT[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            gT[u] = u32x4{pack2_exact(tg[8 * u], tg[8 * u + 1]), pack2_exact(tg[8 * u + 2], tg[8 * u + 3]),
+                          pack2_exact(tg[8 * u + 4], tg[8 * u + 5]), pack2_exact(tg[8 * u + 6], tg[8 * u + 7])};
+            wT[u] = u32x4{pack2_exact(tw[8 * u], tw[8 * u + 1]), pack2_exact(tw[8 * u + 2], tw[8 * u + 3]),
+                          pack2_exact(tw[8 * u + 4], tw[8 * u + 5]), pack2_exact(tw[8 * u + 6], tw[8 * u + 7])};
+          }
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              cacc[a][o] = mfma32(aop[a][u], gT[u], cacc[a][o]);
+              cacc[a][o] = mfma32(yop[a][u], wT[u], cacc[a][o]);
+            }
+        }
+      }
+    }
+    // the four row waves of this block, summed in wave order through LDS
+    __syncthreads();                                       // red of the previous block consumed
+    if (wm > 0) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((((wn * 3 + wm - 1) * 4 + 2 * a + o) * 16) + r) * 64 + l] = cacc[a][o][r];
+    }
+    __syncthreads();
+    if (wm == 0 && bvalid) {
+#pragma unroll
+      for (int s2 = 0; s2 < 3; ++s2)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int o = 0; o < 2; ++o)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cacc[a][o][r] += red[((((wn * 3 + s2) * 4 + 2 * a + o) * 16) + r) * 64 + l];
+      // lane (h, ln) of (a, o) holds dP^T[k = 32a + 8(r/4) + 4h + r%4][j = 32o + ln]; stored as dP[j][k]
+      float* dst = adj.part + ((size_t)tm * adj.nb + bidx) * (ADJ_B * ADJ_B);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int j = 32 * o + ln;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int k = 32 * a + 8 * q + 4 * h;
+            *reinterpret_cast<floatx4*>(dst + j * ADJ_B + k) =
+                floatx4{cacc[a][o][4 * q], cacc[a][o][4 * q + 1], cacc[a][o][4 * q + 2], cacc[a][o][4 * q + 3]};
+          }
+        }
+    }
+  }
+}
+
+// The backward product C = coef[1] * A B^T (bf16 out), or with ADJ the block
+// adjoint of the LCP forward taken straight from the accumulators (C unused).
+template <int BM, int BN, int S, int LSP, bool ADJ = false>
 __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ Bm, int ldb, int M,
-    int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, const float* __restrict__ Eptr) {
+    int N_valid, int N_store, int K, uint16_t* __restrict__ C, int ldc, const float* __restrict__ Eptr,
+    DdAdj adj) {
   constexpr int WM = BM / GWM, WN = BN / GWN, FM = WM / 32, FN = WN / 32;
   constexpr int AI = BM * 8 / GNT, BI = BN * 8 / GNT;     // 16-byte loads per thread per tile
   constexpr int STAGE = (BM + BN) * GBK;                   // bf16 elements per ring stage
@@ -101,6 +305,22 @@ __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int wm = w / GWN, wn = w % GWN;
   const int h = l >> 5, ln = l & 31;
+
+  if constexpr (ADJ) {
+    // the adjoint P fragments of the tile's four blocks (8 KB each, block-major)
+    // go to LDS above the ring now; the main loop's first wait covers them.
+    // Blocks past nb read zeros (offsets past the resource).
+    static_assert(BN == 4 * ADJ_B && S == 2, "fused adjoint: four blocks of 64 per tile, two stages");
+    const __amdgpu_buffer_rsrc_t rF = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(adj.frag), (short)0, (int)(uint32_t)((size_t)adj.nb * ADJ_FRAG * 16), 0x00020000);
+    const int wq = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int chunk = q * GNW + wq;                      // 1 KB chunks 0 .. 31
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rF, (lds_ptr_t)(lds + S * STAGE + chunk * 512), 16, l * 16,
+                                               (int)((uint32_t)(n0 / ADJ_B) * ADJ_FRAG * 16 + chunk * 1024), 0, 0);
+    }
+  }
 
   // load q (< AI: A rows, else B rows) of wave w fills the 64 consecutive
   // 16-byte chunks (q' * GNW + w) * 64 + lane of its matrix in the stage.
@@ -194,6 +414,10 @@ __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
   // ---- epilogue: lane (h, ln) of block (i, j) holds row m0 + wm*WM + 32i + ln,
   // columns n0 + wn*WN + 32j + 16h + r, r < 16.
   const float scale = Eptr[1];
+  if constexpr (ADJ) {
+    dd_adjoint_epilogue(acc, scale, lds, lds + S * STAGE, adj, M, m0, n0, tm, w, l);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * WM + 32 * i + ln;
@@ -637,7 +861,20 @@ hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, i
                                int N, int K, const float* E, uint16_t* C, int ldc, hipStream_t s) {
   const int G = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
   gemm_dd_kernel<DBM, DBN, DS, DLSP><<<G, GNT, gemm_lds_bytes<DBM, DBN, DS>(), s>>>(A, lda, Bm, ldb, M, N, N, K, C,
-                                                                           ldc, E);
+                                                                           ldc, E, DdAdj{});
+  return hipGetLastError();
+}
+
+int dd_adjoint_panels(int M) { return (M + DBM - 1) / DBM; }
+
+hipError_t launch_gemm_dd_adjoint_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M, int N, int K,
+                                       const float* E, const uint16_t* W, const u32x4* frag, const uint32_t* bits,
+                                       float* part, hipStream_t s) {
+  if (N % ADJ_B != 0) return hipErrorInvalidValue;
+  const int G = ((M + DBM - 1) / DBM) * ((N + DBN - 1) / DBN);
+  constexpr size_t lds = gemm_lds_bytes<DBM, DBN, DS>() + 4 * ADJ_FRAG * 16;
+  gemm_dd_kernel<DBM, DBN, DS, DLSP, true><<<G, GNT, lds, s>>>(A, lda, Bm, ldb, M, N, N, K, nullptr, N, E,
+                                                             DdAdj{W, frag, bits, part, N / ADJ_B});
   return hipGetLastError();
 }
 

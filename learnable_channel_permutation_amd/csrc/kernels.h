@@ -31,8 +31,10 @@ struct AdamW {
   float* v;
   float lr, b1, b2, eps, wd, bc1, bc2;
 };
-// dP is either dense [nb][B][B] (seg == nullptr) or the block adjoint's
-// (workgroup, segment) partials described by seg, summed in workgroup order.
+// dP is either dense [nb][B][B] (seg == nullptr), the block adjoint's
+// (workgroup, segment) partials described by seg, summed in workgroup order,
+// or, with seg->tpw < 0, seg->grid row-panel partials [panel][nb][B][B]
+// summed in panel order (the fused dD adjoint).
 // dlogits may be null when opt is given; with opt the kernel also applies
 // AdamW to opt->param (the logits themselves, updated in place).
 hipError_t launch_sinkhorn_bwd(const float* logits, const float* dP, const AdjSplit* seg,
@@ -91,6 +93,16 @@ hipError_t launch_gemm_error_f32(const float* A, int lda, const float* Bm, int l
 // finalisation kernel: -1/E for the Frobenius objective, 1 for the cosine).
 hipError_t launch_gemm_dd_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M,
                                int N, int K, const float* coef, uint16_t* C, int ldc, hipStream_t s);
+// dD GEMM with the block adjoint fused into its epilogue (bf16, B = 64,
+// N % 64 == 0): G = coef[1] A B^T is not stored; each 256-row panel tm writes
+// part[(tm * (N / 64) + b) * 64 * 64] = sum over its rows of
+// G_b^T A_b + W_b^T ((G_b P_b) . M_b) (row-major [j][k]), with frag the
+// adjoint P fragments and bits the block-major mask words. dd_adjoint_panels
+// gives the number of panels.
+int dd_adjoint_panels(int M);
+hipError_t launch_gemm_dd_adjoint_bf16(const uint16_t* A, int lda, const uint16_t* Bm, int ldb, int M, int N, int K,
+                                       const float* coef, const uint16_t* W, const u32x4* frag, const uint32_t* bits,
+                                       float* part, hipStream_t s);
 // f32 dD: C[m][n] = coef[1] sum_t R[m][t] X[t][n]  (X row-major [K][N]).
 hipError_t launch_gemm_dd_f32(const float* R, int ldr, const float* X, int ldx, int M, int N,
                               int K, const float* coef, float* C, int ldc, hipStream_t s);

@@ -415,10 +415,14 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
   if (seg_tpw == 0) {
     ld_block<B>(dP + (size_t)b * B * B, d, w, lr, lc);
   } else {
-    const int g_lo = (b * seg_tpb) / seg_tpw;
-    const int g_hi = min(seg_grid - 1, ((b + 1) * seg_tpb - 1) / seg_tpw);
+    // (workgroup, segment) partials of the block adjoint, or with seg_tpw < 0
+    // one partial per row panel [panel][nb][B][B]
+    const bool panels = seg_tpw < 0;
+    const int g_lo = panels ? 0 : (b * seg_tpb) / seg_tpw;
+    const int g_hi = panels ? seg_grid - 1 : min(seg_grid - 1, ((b + 1) * seg_tpb - 1) / seg_tpw);
     auto slot = [&](int gg) {
-      return dP + ((size_t)gg * seg_maxseg + (b - (gg * seg_tpw) / seg_tpb)) * B * B;
+      return panels ? dP + ((size_t)gg * gridDim.x + b) * B * B
+                    : dP + ((size_t)gg * seg_maxseg + (b - (gg * seg_tpw) / seg_tpb)) * B * B;
     };
 #pragma unroll
     for (int a = 0; a < 4; ++a)

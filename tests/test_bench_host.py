@@ -70,6 +70,21 @@ def test_kernel_work_of_the_bench_layer():
     assert kind == "bytes" and nbytes == 2 * 2048 * 11008 * 2 + 4 * 11008
 
 
+def test_fused_adjoint_work_and_selection():
+    """The bench layer (bf16, B = 64) runs the block adjoint inside the dD
+    GEMM: that kernel's work is the GEMM's 2 Cout Cin T flops plus four
+    products of 2 Cout Cin B flops (W_b P_b, G_b P_b, and the two sums over
+    the rows). The B = 128 layer, fp32 layers and the mask straight-through
+    term keep the separate adjoint."""
+    import lcp_synth
+    spec = lcp_synth.DOWN_PROJ_4096x11008
+    assert bench.fused_adjoint(spec) and not bench.fused_adjoint(spec, mask_ste=True)
+    assert not bench.fused_adjoint(lcp_synth.CONFIGS[3])           # 13824 x 5120, B = 128
+    assert not bench.fused_adjoint(lcp_synth.F32_256x256)
+    kind, flops = bench.kernel_work(spec, ["dD_gemm_adjoint"])["dD_gemm_adjoint"]
+    assert kind == "flops" and flops == 2.0 * 4096 * 11008 * 2048 + 4 * 2.0 * 4096 * 11008 * 64
+
+
 def test_source_identity_hashes_the_library_sources():
     ident = bench.source_identity()
     assert len(ident["csrc_sha16"]) == 16
