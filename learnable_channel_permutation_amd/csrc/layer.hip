@@ -54,9 +54,9 @@ __global__ __launch_bounds__(1024) void colnorm_f32_kernel(const float* __restri
 // and stores the 8 channel rows of Xt (16 bytes each), while summing squares
 // for its 8 channels. Two tiles are in flight per wave. Column sums are
 // reduced over the 16 lanes of a column block (one DPP row) and then over the
-// 4 waves (LDS), in a fixed order. X is read and Xt written with
-// non-temporal accesses: neither is touched again until much later in the
-// step, and keeping them out of the caches leaves the weights there.
+// 4 waves (LDS), in a fixed order. X is read and Xt written through the
+// caches: the error GEMM reads X again soon after, and finds much of it
+// there.
 __device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8]) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -91,8 +91,7 @@ __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int row = t0 + 8 * rb + e;
-      r[e] = (cok && row < T) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + (size_t)row * cin + c0))
-                              : u32x4{0u, 0u, 0u, 0u};
+      r[e] = (cok && row < T) ? *reinterpret_cast<const u32x4*>(X + (size_t)row * cin + c0) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto consume = [&](int t0, const u32x4 (&r)[8]) {
@@ -110,7 +109,7 @@ __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __
       transpose8x8(r, o);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        __builtin_nontemporal_store(o[c], reinterpret_cast<u32x4*>(Xt + (size_t)(c0 + c) * pitch + t0 + 8 * rb));
+        *reinterpret_cast<u32x4*>(Xt + (size_t)(c0 + c) * pitch + t0 + 8 * rb) = o[c];
     }
   };
 
