@@ -461,13 +461,12 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
   __syncthreads();
 
   // Z^k for this lane's elements: z0 minus the offsets of iterations < k, in
-  // the forward's order (row offset, then column offset, per iteration)
-  auto rebuild = [&](int k, float (&v)[4][CPL]) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) v[a][c] = z0[a][c];
-    for (int i = 0; i < k; ++i) {
+  // the forward's order (row offset, then column offset, per iteration).
+  // Z^kc (kc = ceil(L/2)) is kept as a checkpoint, and an iterate past it
+  // continues from there: the same operations on the same values, about
+  // half the passes (the reverse sweep would otherwise cost O(L^2) of them).
+  auto advance = [&](int from, int to, float (&v)[4][CPL]) {
+    for (int i = from; i < to; ++i) {
       const floatx4 r = *reinterpret_cast<const floatx4*>(sh_off + (2 * i) * B + row0);
       float cv[CPL];
       ld_cols<CPL>(sh_off + (2 * i + 1) * B + lc * CPL, cv);
@@ -476,6 +475,21 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
 #pragma unroll
         for (int c = 0; c < CPL; ++c) v[a][c] = (v[a][c] - r[a]) - cv[c];
     }
+  };
+  const int kc = (iters + 1) / 2;
+  float zc[4][CPL];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) zc[a][c] = z0[a][c];
+  advance(0, kc, zc);
+  auto rebuild = [&](int k, float (&v)[4][CPL]) {
+    const bool past = k >= kc;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[a][c] = past ? zc[a][c] : z0[a][c];
+    advance(past ? kc : 0, k, v);
   };
 
   float g[4][CPL];
