@@ -330,6 +330,33 @@ def test_step_small(ci, cout, cin, T):
     _check_step(lay, spec, got)
 
 
+FUSED = [
+    # (cout, cin, T) of the 4096 x 11008 layer's kind (bf16, B = 64): the dD
+    # GEMM takes the block adjoint in its epilogue, 256 x 256 tiles of four
+    # blocks. Exactly one tile; rows one short of a panel with a last column
+    # tile holding one valid block (of four); three valid blocks in the last
+    # tile; a last panel of one row with wave-half blocks past Cin; a single
+    # K step (T = 1); four panels by four column tiles.
+    (256, 256, 64),
+    (255, 320, 96),
+    (511, 448, 130),
+    (769, 192, 70),
+    (300, 256, 1),
+    (1024, 1024, 128),
+]
+
+
+@pytest.mark.parametrize("cout,cin,T", FUSED)
+def test_step_fused_adjoint_tiling(cout, cin, T):
+    """Tilings of the dD GEMM with the fused block adjoint: ragged row
+    panels, column tiles with fewer than four valid blocks, one K step."""
+    spec = lcp_synth.DOWN_PROJ_4096x11008
+    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
+    say("step fused adjoint tiling", cout, cin, T)
+    got = _run_step(lay, spec)
+    _check_step(lay, spec, got)
+
+
 TINY = [
     # (config index, cout, cin, T): one output row, one token, one block,
     # sizes one past a tile boundary
