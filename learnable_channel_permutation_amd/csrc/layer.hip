@@ -52,7 +52,8 @@ __global__ __launch_bounds__(1024) void colnorm_f32_kernel(const float* __restri
 // each 128-token x 32-channel tile: it loads the 8 token rows (16 bytes
 // each), transposes the block in registers (one v_perm_b32 per output word)
 // and stores the 8 channel rows of Xt (16 bytes each), while summing squares
-// for its 8 channels. Two tiles are in flight per wave. Column sums are
+// for its 8 channels. Four tiles are in flight per wave (all of a wave's
+// tiles at 2,048 tokens). Column sums are
 // reduced over the 16 lanes of a column block (one DPP row) and then over the
 // 4 waves (LDS), in a fixed order. X is read and Xt written through the
 // caches: the error GEMM reads X again soon after, and finds much of it
@@ -113,9 +114,19 @@ __global__ __launch_bounds__(256) void layer_init_bf16_kernel(const uint16_t* __
     }
   };
 
-  // wave w covers token tiles w, w + 4, w + 8, ... (128 tokens each), two at a time
-  u32x4 ra[8], rb2[8];
+  // wave w covers token tiles w, w + 4, w + 8, ... (128 tokens each), four at a time
+  u32x4 ra[8], rb2[8], rc[8], rd[8];
   int t0 = 128 * w;
+  for (; t0 + 1536 < t_end; t0 += 2048) {
+    load(t0, ra);
+    load(t0 + 512, rb2);
+    load(t0 + 1024, rc);
+    load(t0 + 1536, rd);
+    consume(t0, ra);
+    consume(t0 + 512, rb2);
+    consume(t0 + 1024, rc);
+    consume(t0 + 1536, rd);
+  }
   for (; t0 + 512 < t_end; t0 += 1024) {
     load(t0, ra);
     load(t0 + 512, rb2);
