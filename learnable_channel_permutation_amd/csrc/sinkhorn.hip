@@ -433,7 +433,7 @@ __global__ __launch_bounds__(SkGeom<B>::THREADS) void sinkhorn_bwd_kernel(
       float q[4][4][CPL];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (g0 + k <= g_hi) ld_block<B>(slot(g0 + k), q[k], w, lr, lc);
+        if (g0 + k <= g_hi) ld_block<B, true>(slot(g0 + k), q[k], w, lr, lc);   // read once: non-temporal
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (g0 + k <= g_hi) {
