@@ -109,19 +109,27 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
 }
 
 // ---- 2:4 sparse GEMM ----------------------------------------------------------------
-// Y[t][o] = sum_k Ws[o][k] Xp[t][k]. 256 (rows o) x 128 (tokens t) tiles, 8
-// waves in a 4 x 2 layout (each wave 64 x 64: 2 x 2 sparse MFMA blocks), K
-// steps of 64 positions. A ring stage holds the 16 weight fragments of one
-// step (16 KB, lane order, linear LDS reads), their position words (2 KB)
-// and the 128 x 64 activation tile (16 KB, rows swizzled as in the dense
-// GEMM), all moved with direct-to-LDS loads; four stages (136 KB of LDS)
-// keep three tiles in flight per CU. The ring is software-pipelined
-// like the dense error GEMM: the five loads of tile kt + RS - 1 go out one at a
-// time between the first sub-step's MFMAs of step kt (a burst right after the
-// barrier stalls every wave on the vector-memory queue), and each step's
-// barrier sits before its second 32-position sub-step, whose MFMAs run from
-// registers while the first fragments of the next stage are read.
-constexpr int SP_BM = 256, SP_BN = 128, SP_NT = 512, SP_RS = 4, SP_NL = 5;
+// Y[t][o] = sum_k Ws[o][k] Xp[t][k]. 256 (rows o) x 128 (tokens t) tiles (a
+// 4096 x 2048 output is one round of 256 workgroups), 8 waves, K steps of 64
+// positions. The two 32-position halves of every K step go to two groups of
+// four waves (the K sum is split inside the workgroup): wave v of group g
+// computes rows 128 (v / 2) + [0, 128) and tokens 64 (v % 2) + [0, 64) of the
+// tile (4 x 2 sparse MFMA blocks) over half g of every step, and at the end
+// the groups exchange half of their accumulators through LDS, each adding
+// and storing one half. A 128 x 64 wave tile reads 9 KB of fragments for its
+// 8 MFMAs of a step; 64 x 64 tiles over both halves would read 13 KB.
+// A ring stage holds the 16 weight fragments of one step (16 KB, lane order,
+// linear LDS reads), their position words (2 KB) and the 128 x 64 activation
+// tile (16 KB, rows swizzled as in the dense GEMM), all moved with
+// direct-to-LDS loads; four stages (136 KB of LDS) keep three tiles in flight
+// per CU. Pipeline of step kt: the wave's first two MFMAs, the barrier, then
+// the next stage's fragments are read into the second register set while the
+// last six MFMAs run from the first; the five loads of tile kt + RS - 1 go
+// out one at a time between the eight MFMAs (a burst right after the barrier
+// stalls every wave on the vector-memory queue).
+// SP_NPRE: MFMAs of a step before its barrier; SP_LSPAN: MFMAs the five
+// loads are spread over
+constexpr int SP_BM = 256, SP_BN = 128, SP_NT = 512, SP_RS = 4, SP_NL = 5, SP_NPRE = 2, SP_LSPAN = 8;
 constexpr int SP_A1 = (SP_BM / 32) * 2 * 1024, SP_M1 = (SP_BM / 32) * 256, SP_B1 = SP_BN * 64 * 2;
 constexpr int SP_STAGE = SP_A1 + SP_M1 + SP_B1;
 constexpr int SP_MOFF = SP_A1, SP_BOFF = SP_A1 + SP_M1;
@@ -148,20 +156,21 @@ __device__ __forceinline__ void sp_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int RS>
+template <int RS, int NPRE, int LSPAN>
 __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restrict__ vals,
                                                           const uint32_t* __restrict__ meta,
                                                           const uint16_t* __restrict__ Xp, int T, int cout,
                                                           int cin, uint16_t* __restrict__ Y) {
-  constexpr int FM = 2, FN = 2, NM = FM * FN, WM = 64, WN = 64, NL = SP_NL;
-  static_assert(RS >= 3 && (RS - 2) * NL < 64, "ring depth");
+  constexpr int FM = 4, FN = 2, NM = FM * FN, WM = 128, WN = 64, NL = SP_NL;
+  static_assert(RS >= 3 && RS % 2 == 0 && (RS - 2) * NL < 64, "ring depth");
+  static_assert(8 * FM * 4 * 64 * 16 <= RS * SP_STAGE, "the accumulator exchange fits in the ring");
   extern __shared__ __attribute__((aligned(16))) unsigned char sp_lds[];
   const int tiles_m = (cout + SP_BM - 1) / SP_BM, tiles_n = (T + SP_BN - 1) / SP_BN;
   int tm, tn;
   sp_tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * SP_BM, n0 = tn * SP_BN;
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int g = __builtin_amdgcn_readfirstlane(w >> 2), v = w & 3, wm = v >> 1, wn = v & 1;
   const int h = l >> 5, ln = l & 31;
   const int KF = cin / 32, NK = (cin + 63) / 64, RG = cout / 32;
 
@@ -219,70 +228,86 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
-  // fragments of 32-position sub-step p of a stage into register set p; the
-  // position word is kept whole (sub-step p uses its half p)
+  // fragments of half g of a stage, two register sets (the next stage is read
+  // while the current one still feeds MFMAs); the position word of a row
+  // group is read as the 16-bit half g
   u32x4 fa[2][FM];
   bf16x16 fb[2][FN];
   uint32_t fm[2][FM];
-  auto rd = [&](int stage, int p) {
+  int boff[FN][2];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int row = wn * WN + 32 * j + ln;
+    boff[j][0] = sp_swz(row, 4 * g + h);
+    boff[j][1] = sp_swz(row, 4 * g + 2 + h);
+  }
+  auto rd = [&](int stage, auto SET) {
+    constexpr int S = decltype(SET)::value;
     const unsigned char* sb = sp_lds + stage * SP_STAGE;
     const u32x4* LA = reinterpret_cast<const u32x4*>(sb);
-    const uint32_t* LM = reinterpret_cast<const uint32_t*>(sb + SP_MOFF);
+    const uint16_t* LM = reinterpret_cast<const uint16_t*>(sb + SP_MOFF);
     const uint16_t* LB = reinterpret_cast<const uint16_t*>(sb + SP_BOFF);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      fa[p][i] = LA[((wm * FM + i) * 2 + p) * 64 + l];
-      fm[p][i] = LM[(wm * FM + i) * 64 + l];
+      fa[S][i] = LA[((wm * FM + i) * 2 + g) * 64 + l];
+      fm[S][i] = LM[((wm * FM + i) * 64 + l) * 2 + g];
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int row = wn * WN + 32 * j + ln;
-      const u32x4 b0 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + h)]);
-      const u32x4 b1 = *reinterpret_cast<const u32x4*>(&LB[sp_swz(row, 4 * p + 2 + h)]);
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(&LB[boff[j][0]]);
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(&LB[boff[j][1]]);
       typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-      fb[p][j] = __builtin_bit_cast(bf16x16, u32x8{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w});
+      fb[S][j] = __builtin_bit_cast(bf16x16, u32x8{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w});
     }
   };
-  // the instruction's index-set field picks half p of the position word
-  auto mma = [&](int p, int m) {
-    const int i = m / FN, j = m % FN;
-    const int idx = (int)fm[p][i];
-    if (p == 0)
-      acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(fa[p][i]), fb[p][j], acc[i][j], idx, 0, 0);
-    else
-      acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(fa[p][i]), fb[p][j], acc[i][j], idx, 0, 1);
+  // MFMA m of a step: block (m % FM, m / FM); the index-set field stays 0
+  // since the position word already holds half g in its low bits
+  auto mma = [&](auto SET, int m) {
+    constexpr int S = decltype(SET)::value;
+    const int i = m % FM, j = m / FM;
+    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(fa[S][i]), fb[S][j], acc[i][j], (int)fm[S][i], 0, 0);
   };
-  // step on stage `stage` (sub-step 0 fragments already in registers): with `load`
-  // the tile of K step ks goes to stage `lstage`; with `next` the first
-  // fragments of stage `nstage` are read after the barrier. WAIT (steady
-  // state): the loads of the RS - 2 tiles after the next one may stay in flight.
-  auto step = [&](int stage, int lstage, int ks, int nstage, bool load, bool next, auto WAIT, auto TAIL) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);                    // sub-step 0's fragments are in
-    __builtin_amdgcn_sched_barrier(0);
-    rd(stage, 1);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
+  // step on stage `stage`, its fragments in set SET: with `load` the tile of K
+  // step ks goes to stage `lstage` (its slot was last read before the previous
+  // barrier); with `next` the fragments of stage `nstage` are read into the
+  // other set after the barrier. WAIT (steady state): before the barrier the
+  // wave's loads of the next tile must be done, those of the RS - 3 tiles
+  // after it and the PRE loads of this step's tile issued so far may stay in
+  // flight (vmcnt counts in issue order).
+  constexpr int PRE = [] {                                 // loads issued before the barrier
+    int n = 0;
+    for (int o = 0; o < NL; ++o) n += (o * LSPAN / NL < NPRE);
+    return n;
+  }();
+  auto step = [&](auto SET, int stage, int lstage, int ks, int nstage, bool load, bool next, auto WAIT, auto TAIL) {
+    constexpr int S = decltype(SET)::value;
+    auto mfma_loads = [&](int m) {
 #pragma unroll
       for (int o = 0; o < NL; ++o)
-        if (load && o * NM / NL == m) {
+        if (load && o * LSPAN / NL == m) {
           __builtin_amdgcn_sched_barrier(0);
           issue_one(lstage, ks, o, TAIL);
           __builtin_amdgcn_sched_barrier(0);
         }
-      mma(0, m);
-    }
+      mma(SET, m);
+    };
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(WAIT)::value) sp_wait_vmcnt<(RS - 2) * NL>();
+#pragma unroll
+    for (int m = 0; m < NPRE; ++m) mfma_loads(m);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(WAIT)::value) sp_wait_vmcnt<(RS - 3) * NL + PRE>();
     else sp_wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): this stage's reads are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (next) rd(nstage, 0);
+    if (next) rd(nstage, std::integral_constant<int, 1 - S>{});
     __builtin_amdgcn_sched_barrier(0);                     // nothing here waits for those reads
 #pragma unroll
-    for (int m = 0; m < NM; ++m) mma(1, m);
+    for (int m = NPRE; m < NM; ++m) mfma_loads(m);
     __builtin_amdgcn_sched_barrier(0);
   };
+  constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
 
   // prologue: tiles 0 .. RS - 2 (a tile past K reads zeros and is never multiplied)
 #pragma unroll
@@ -291,36 +316,67 @@ __global__ __launch_bounds__(SP_NT, 1) void spgemm_kernel(const u32x4* __restric
     for (int o = 0; o < NL; ++o) issue_one(s, s, o, std::true_type{});
   sp_wait_vmcnt<(RS - 2) * NL>();
   __builtin_amdgcn_s_barrier();
-  rd(0, 0);
+  rd(0, S0);
   int kt = 0;
-  // RS steady-state steps; they load K steps up to kt + 2 RS - 2 < NK - 1,
-  // never the last one
+  // RS steady-state steps (RS is even: step kt uses set kt % 2); they load K
+  // steps up to kt + 2 RS - 2 < NK - 1, never the last one
   for (; kt + 2 * RS - 1 < NK; kt += RS) {
 #pragma unroll
-    for (int s = 0; s < RS; ++s)
-      step(s, (s + RS - 1) % RS, kt + s + RS - 1, (s + 1) % RS, true, true, std::true_type{}, std::false_type{});
+    for (int s = 0; s < RS; s += 2) {
+      step(S0, s, (s + RS - 1) % RS, kt + s + RS - 1, s + 1, true, true, std::true_type{}, std::false_type{});
+      step(S1, s + 1, s, kt + s + RS, (s + 2) % RS, true, true, std::true_type{}, std::false_type{});
+    }
   }
-  for (; kt < NK; ++kt)                                    // the last steps, all loads retired at each barrier
-    step(kt % RS, (kt + RS - 1) % RS, kt + RS - 1, (kt + 1) % RS, kt + RS - 1 < NK, kt + 1 < NK,
+  for (; kt < NK; kt += 2) {                               // the last steps, all loads retired at each barrier
+    step(S0, kt % RS, (kt + RS - 1) % RS, kt + RS - 1, (kt + 1) % RS, kt + RS - 1 < NK, kt + 1 < NK,
          std::false_type{}, std::true_type{});
+    if (kt + 1 < NK)
+      step(S1, (kt + 1) % RS, kt % RS, kt + RS, (kt + 2) % RS, kt + RS < NK, kt + 2 < NK, std::false_type{},
+           std::true_type{});
+  }
   sp_wait_vmcnt<0>();                                      // the zero tiles of a short K
+  __syncthreads();                                         // every wave is done with the ring
 
-  // lane (h, ln) of block (i, j): token n0 + wn*64 + 32j + ln, rows
-  // m0 + wm*64 + 32i + 16h + r (r < 16)
+  // exchange: group g hands its blocks of column 1 - g to the other group and
+  // adds the other group's blocks of column g to its own (x + y = y + x, so
+  // both halves get the same sum as any fixed order)
+  floatx4* xl = reinterpret_cast<floatx4*>(sp_lds);
+  auto put = [&](auto J) {
+    constexpr int j = decltype(J)::value;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int o = m0 + wm * WM + 32 * i + 16 * h;
-    if (o >= cout) continue;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int tk = n0 + wn * WN + 32 * j + ln;
-      if (tk >= T) continue;
-      const floatx16 a = acc[i][j];
+      for (int q = 0; q < 4; ++q)
+        xl[(((g * 4 + v) * FM + i) * 4 + q) * 64 + l] =
+            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+  };
+  auto take_store = [&](auto J) {
+    constexpr int j = decltype(J)::value;
+    const int tk = n0 + wn * WN + 32 * j + ln;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      floatx16 a = acc[i][j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 x = xl[((((1 - g) * 4 + v) * FM + i) * 4 + q) * 64 + l];
+        a[4 * q] += x[0];
+        a[4 * q + 1] += x[1];
+        a[4 * q + 2] += x[2];
+        a[4 * q + 3] += x[3];
+      }
+      // lane (h, ln): token tk, rows m0 + wm*128 + 32i + 16h + r (r < 16)
+      const int o = m0 + wm * WM + 32 * i + 16 * h;
+      if (o >= cout || tk >= T) continue;
       u32x4* dst = reinterpret_cast<u32x4*>(Y + (size_t)tk * cout + o);
       dst[0] = u32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7])};
       dst[1] = u32x4{pack2(a[8], a[9]), pack2(a[10], a[11]), pack2(a[12], a[13]), pack2(a[14], a[15])};
     }
-  }
+  };
+  if (g == 0) put(S1);
+  else put(S0);
+  __syncthreads();
+  if (g == 0) take_store(S0);
+  else take_store(S1);
 }
 
 // ---- launchers ----------------------------------------------------------------------
@@ -344,7 +400,7 @@ hipError_t launch_gather(const uint16_t* X, int T, int cin, int B, const int* pe
 hipError_t launch_spgemm(const u32x4* vals, const uint32_t* meta, const uint16_t* Xp, int T, int cout, int cin,
                          uint16_t* Y, hipStream_t s) {
   const int G = ((cout + SP_BM - 1) / SP_BM) * ((T + SP_BN - 1) / SP_BN);
-  spgemm_kernel<SP_RS><<<G, SP_NT, SP_RS * SP_STAGE, s>>>(vals, meta, Xp, T, cout, cin, Y);
+  spgemm_kernel<SP_RS, SP_NPRE, SP_LSPAN><<<G, SP_NT, SP_RS * SP_STAGE, s>>>(vals, meta, Xp, T, cout, cin, Y);
   return hipGetLastError();
 }
 
