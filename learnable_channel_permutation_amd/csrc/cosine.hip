@@ -23,10 +23,22 @@ __global__ __launch_bounds__(64) void cosine_finalize_kernel(const float* __rest
                                                              const float* __restrict__ y2p,
                                                              float* __restrict__ coef,
                                                              float* __restrict__ err) {
+  // eight far-memory loads of each array in flight per lane, added in order
+  // (a slot past n adds +0)
   double r = 0.0, a = 0.0;
-  for (int i = threadIdx.x; i < n; i += 64) {
-    r += (double)part[i];
-    a += (double)party[i];
+  for (int i = threadIdx.x; i < n; i += 512) {
+    float vr[8], va[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool in = i + 64 * q < n;
+      vr[q] = in ? part[i + 64 * q] : 0.f;
+      va[q] = in ? party[i + 64 * q] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      r += (double)vr[q];
+      a += (double)va[q];
+    }
   }
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) {

@@ -802,23 +802,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // E = sqrt(sum of partials), summed in a fixed order by one wave: lane l adds
 // part[l], part[l + 64], ... in order, then the lanes are combined by a fixed
 // butterfly. The partials were just written by workgroups on every XCD, so
-// each read is a far-memory round trip: a lane issues four of them before it
-// adds any (the order of the additions is unchanged). E_ws[0] = E and E_ws[1] = -1/E (0 when E == 0), the factor the
+// each read is a far-memory round trip: a lane issues eight of them before it
+// adds any, in the same order (a slot past n adds +0, which leaves the sum
+// unchanged). E_ws[0] = E and E_ws[1] = -1/E (0 when E == 0), the factor the
 // dD epilogue applies (dE/dR = R / E, dE/dW_tilde = -(R / E) X). With
 // sum_only the plain sum is written to err (E_ws unused).
 __global__ __launch_bounds__(64) void error_finalize_kernel(const float* __restrict__ part, int n,
                                                             float* __restrict__ E_ws,
                                                             float* __restrict__ err, int sum_only) {
   float s = 0.f;
-  int i = threadIdx.x;
-  for (; i + 192 < n; i += 256) {
-    const float a = part[i], b = part[i + 64], c = part[i + 128], d = part[i + 192];
-    s += a;
-    s += b;
-    s += c;
-    s += d;
+  for (int i = threadIdx.x; i < n; i += 512) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (i + 64 * q < n) ? part[i + 64 * q] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
   }
-  for (; i < n; i += 64) s += part[i];
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) s += shfl_xor(s, x);
   if (threadIdx.x == 0) {
