@@ -309,15 +309,17 @@ __global__ __launch_bounds__(GNT, 1) void gemm_dd_kernel(
   if constexpr (ADJ) {
     // the adjoint P fragments of the tile's four blocks (8 KB each, block-major)
     // go to LDS above the ring now; the main loop's first wait covers them.
-    // Blocks past nb read zeros (offsets past the resource).
+    // Chunks of blocks past nb take the per-lane offset past the resource and
+    // read zeros (those blocks are never used).
     static_assert(BN == 4 * ADJ_B && S == 2, "fused adjoint: four blocks of 64 per tile, two stages");
     const __amdgpu_buffer_rsrc_t rF = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u32x4*>(adj.frag), (short)0, (int)(uint32_t)((size_t)adj.nb * ADJ_FRAG * 16), 0x00020000);
     const int wq = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int chunk = q * GNW + wq;                      // 1 KB chunks 0 .. 31
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rF, (lds_ptr_t)(lds + S * STAGE + chunk * 512), 16, l * 16,
+      const int chunk = q * GNW + wq;                      // 1 KB chunks 0 .. 31, 8 per block
+      const uint32_t vo = (n0 / ADJ_B + chunk / 8 < adj.nb) ? (uint32_t)(l * 16) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rF, (lds_ptr_t)(lds + S * STAGE + chunk * 512), 16, (int)vo,
                                                (int)((uint32_t)(n0 / ADJ_B) * ADJ_FRAG * 16 + chunk * 1024), 0, 0);
     }
   }
