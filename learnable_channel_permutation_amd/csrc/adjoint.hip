@@ -110,7 +110,9 @@ __global__ __launch_bounds__(AdjGeom<B>::THREADS, (B == 128) ? 1 : 2) void adjoi
   unsigned char* rings = adj_lds + Gm::FRAG * 16;
   float* red = reinterpret_cast<float*>(rings);
 
-  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  // the wave index as a uniform value: the slot, the ring address and the
+  // loads' scalar offsets derived from it then stay in scalar registers
+  const int t = threadIdx.x, l = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h = l >> 5, n = l & 31;
   const int slot = w / WS;          // row tile slot of this wave
   const int half = w % WS;          // position blocks a = half * NA + ai
