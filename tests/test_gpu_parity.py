@@ -321,6 +321,46 @@ SMALL = [
 ]
 
 
+MASK_CASES = [
+    # (config index, cout, cin, T, N, M): every N:M selection path of the
+    # fused permute (M = 4 with N compiled in, M = 8 at run time, the fp32
+    # kernel) at B = 32, 64 and 128, ragged row counts
+    (0, 70, 256, 64, 2, 4),
+    (2, 300, 512, 130, 2, 4),
+    (2, 257, 384, 96, 1, 4),
+    (2, 257, 384, 96, 3, 4),
+    (2, 257, 384, 96, 4, 8),
+    (3, 270, 512, 160, 4, 8),
+    (3, 100, 256, 64, 2, 4),
+]
+
+
+@pytest.mark.parametrize("ci,cout,cin,T,N,M", MASK_CASES)
+def test_step_mask_is_nm_rule_of_its_scores(ci, cout, cin, T, N, M):
+    """The fused permute's keep decision, bit for bit: the step's mask is the
+    oracle's N:M rule (PermLLM blog 2.1, ties to the lower position) applied
+    to the importance scores S_hat = (|W| n) P that the same MFMA (or fp32
+    FMA) sequence produces, taken from the importance-only permute on the
+    step's own P and column norms. The step tests compare the mask with the
+    oracle's float64 scores; this one isolates the selection itself."""
+    spec = lcp_synth.CONFIGS[ci]
+    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    W, X = up(lay.W, tdt), up(lay.X, tdt)
+    lg = up(lay.logits)
+    say("step mask vs its scores", spec.name, cout, cin, T, N, M)
+    s = lcp.LayerSession(W, X, spec.B, spec.iters, spec.tau, N, M)
+    P = torch.empty_like(lg)
+    bits = empty_bits(cout, cin)
+    s.forward(lg, P_out=P, bits_out=bits)
+    S = torch.empty((cout, cin), dtype=torch.float32, device=DEV)
+    L.lcp_permute(W, P, spec.B, S, colscale=s.norms)
+    torch.cuda.synchronize()
+    want = oracle.pack_bits(oracle.nm_mask(down(S), N, M))
+    got = bits_down(bits)
+    assert np.array_equal(got, want), bit_agreement(got, want, cout * cin)
+
+
 @pytest.mark.parametrize("ci,cout,cin,T", SMALL)
 def test_step_small(ci, cout, cin, T):
     spec = lcp_synth.CONFIGS[ci]
