@@ -108,7 +108,11 @@ __global__ __launch_bounds__((PermGeom<B, MODE>::THREADS)) void permute_bf16_ker
   const int h = l >> 5, n = l & 31;
   const int tpb = (rows + 31) / 32;
   const int total = (cin / B) * tpb;
-  const int t_begin = blockIdx.x * tpw;
+  // workgroup g runs on XCD g % 8: consecutive tile ranges go to one XCD, so
+  // the few workgroups that share a block fetch its P fragments into one L2
+  // (the grid is a multiple of 8; ranges past the end are empty)
+  const int g = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int t_begin = g * tpw;
   const int t_end = min(total, t_begin + tpw);
 
   for (int seg = t_begin; seg < t_end;) {
@@ -378,7 +382,7 @@ static hipError_t perm_bf16_launch(const uint16_t* A, int rows, int cin, const f
   const int total = (cin / B) * ((rows + 31) / 32);
   int grid = perm_grid(B, MODE);
   const int tpw = (total + grid - 1) / grid;
-  grid = (total + tpw - 1) / tpw;
+  grid = ((total + tpw - 1) / tpw + 7) / 8 * 8;          // whole XCD rounds
   permute_bf16_kernel<B, MODE, M, NK><<<grid, G::THREADS, G::LDS, s>>>(A, rows, cin, colscale, P, transposeP,
                                                                     gfrag, tpw, out, out_f32, bits, N);
   return hipGetLastError();
