@@ -4,6 +4,8 @@ the C ABI, on seeded inputs. Tolerances: Sinkhorn per entry 1e-5 relative +
 GEMM residual and error 1e-2 relative; gradients against the oracle's backward
 taken on the GPU's mask (held constant): 1e-2 relative (Frobenius) over the
 whole tensor and 2e-2 for every B x B block."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -99,6 +101,43 @@ def test_sinkhorn_backward(B, iters, tau):
     P, tr = oracle.sinkhorn(lg.astype(np.float64), tau64, iters, trace=True)
     ref = oracle.sinkhorn_adjoint(dP.astype(np.float64), P, tr, tau64)
     assert rel_fro(down(d_out), ref) < 1e-4
+
+
+@pytest.mark.parametrize("B", [32, 64, 128])
+def test_sinkhorn_at_the_iteration_cap(B):
+    """iters * B = LCP_MAX_ITERS_B, the largest count the kernels accept (the
+    reverse pass keeps the offsets of every iteration of a block in LDS):
+    the forward per entry and the backward against the oracle. The iterates
+    are rebuilt from 2L offsets, each subtraction rounding by up to
+    |Z| 2^-24 (base 2), which bounds the extra relative error by
+    2L |Z| 2^-24 ln 2 (about 3e-5 at L = 256 here)."""
+    iters, nb, tau = L.LCP_MAX_ITERS_B // B, 5, 1.0
+    lg = lcp_synth.random_logits(500 + B, nb, B, scale=0.5)
+    say("sinkhorn at the iteration cap", B, iters)
+    d_lg = up(lg)
+    d_P = torch.empty_like(d_lg)
+    L.lcp_sinkhorn(d_lg, d_P, iters, tau)
+    dP = lcp_synth.random_matrix(600 + B, (nb, B, B))
+    d_out = torch.empty((nb, B, B), dtype=torch.float32, device=DEV)
+    L.lcp_sinkhorn_bwd(d_lg, up(dP), iters, tau, d_out)
+    torch.cuda.synchronize()
+    P, tr = oracle.sinkhorn(lg.astype(np.float64), np.float64(tau), iters, trace=True)
+    drift = 2 * iters * (np.max(np.abs(lg)) / tau * np.log2(np.e)) * 2.0 ** -24 * np.log(2)
+    got = down(d_P)
+    assert np.all(np.abs(got - P) <= _sink_tol(P) + drift * np.abs(P)), np.max(np.abs(got - P) / (np.abs(P) + 1e-9))
+    want = oracle.sinkhorn_adjoint(dP.astype(np.float64), P, tr, np.float64(tau))
+    assert rel_fro(down(d_out), want) < 1e-4 + drift
+
+
+def test_step_at_the_iteration_cap():
+    """A whole bf16 step (B = 64) with iters * B = LCP_MAX_ITERS_B: the
+    forward's offsets and the backward's LDS copy of them at their largest,
+    against the float64 oracle with the same tolerances as every step."""
+    spec = dataclasses.replace(lcp_synth.CONFIGS[2], iters=L.LCP_MAX_ITERS_B // 64)
+    lay = lcp_synth.make_layer(spec, cout=96, cin=128, T=64)
+    say("step at the iteration cap", spec.iters)
+    got = _run_step(lay, spec)
+    _check_step(lay, spec, got)
 
 
 # ---------------------------------------------------------------- N:M mask --
