@@ -595,9 +595,13 @@ def test_step_hardened(ci, cout, cin, T):
     """Hardened forward (Method 2) and straight-through backward against the
     oracle: the hard P exactly, the mask, E and the gradient."""
     spec = lcp_synth.CONFIGS[ci]
-    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
-    lg, Pi = lcp_synth.planted_logits(500 + ci, cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
     say("step hardened", spec.name, cout, cin, T)
+    _check_hardened(spec, cout, cin, T, 500 + ci)
+
+
+def _check_hardened(spec, cout, cin, T, seed):
+    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
+    lg, Pi = lcp_synth.planted_logits(seed, cin // spec.B, spec.B, peak=1.5, noise_std=0.3)
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
     s = lcp.LayerSession(up(lay.W, tdt), up(lay.X, tdt), spec.B, spec.iters, spec.tau, spec.N, spec.M,
                          harden=True)
@@ -615,6 +619,19 @@ def test_step_hardened(ci, cout, cin, T):
     assert abs(float(err.item()) - fw["E"]) / fw["E"] < 1e-2
     _, bw = oracle_backward_on_mask(lay, spec, lg, bits_down(bits), hard=True)
     check_gradient(down(dl), bw["dlogits"])
+
+
+@pytest.mark.parametrize("cout,cin,T", [(300, 256, 130), (33, 96, 65)])
+def test_step_bf16_block32(cout, cin, T):
+    """bf16 layers with B = 32 (the bench layer's distributions, 2:4): the
+    B = 32 Sinkhorn, permute and separate adjoint of a bf16 step, soft and
+    hardened, against the oracle with the same tolerances as every step."""
+    spec = dataclasses.replace(lcp_synth.CONFIGS[2], B=32)
+    lay = lcp_synth.make_layer(spec, cout=cout, cin=cin, T=T)
+    say("step bf16 B = 32", cout, cin, T)
+    got = _run_step(lay, spec)
+    _check_step(lay, spec, got)
+    _check_hardened(spec, cout, cin, T, 700 + cout)
 
 
 def test_step_hardened_full_size_bench_layer():
